@@ -1,0 +1,373 @@
+"""Pins of the float64 oracle to facts fixed by the pages and by mathematics.
+
+Each test is chosen so that a plausible slip in the oracle (a dropped term, a wrong
+sign or index, a transposed operand, a wrong tie rule) fails at least one of them:
+hand-worked fixtures under tests/golden/, closed forms, brute force on tiny inputs,
+reductions to library routines, and invariants.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from contextual_sparsity_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _num(v):
+    if isinstance(v, str):
+        return {"nan": math.nan, "-inf": -math.inf, "inf": math.inf, "-0.0": -0.0,
+                "ln3": math.log(3.0)}[v]
+    return v
+
+
+def _arr(v, dtype=np.float64):
+    if isinstance(v, list):
+        return np.array([_arr(e, dtype) for e in v], dtype=dtype) if v and isinstance(v[0], list) \
+            else np.array([_num(e) for e in v], dtype=dtype)
+    return _num(v)
+
+
+def _rel(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    den = np.linalg.norm(b)
+    return np.linalg.norm(a - b) / (den if den > 0 else 1.0)
+
+
+def _tiny(B=1, dtype="f32", seed=3, **kw):
+    base = dict(d=24, N=40, h=4, dh=6, n=7, r=10, B=B, dtype=dtype)
+    base.update(kw)
+    s = synth.LayerShape(**base)
+    L = synth.make_layer(s, seed, 0)
+    P = synth.make_predictors(s, seed, 0)
+    x = synth.make_input(s, seed)
+    np_ = lambda t: t.numpy()
+    LW = O.LayerWeights(**{k: np_(v) for k, v in L.items()})
+    PW = O.PredictorWeights(**{k: np_(v) for k, v in P.items()})
+    return s, LW, PW, x.numpy()
+
+
+# ------------------------------------------------------------------------------ keep counts
+def test_keep_count_configuration_values():
+    # OPT-125m shape: 5% of 3072 neurons, about 20% of 12 heads.
+    assert O.keep_count(5, 3072) == 154
+    assert O.keep_count(20, 12) == 3
+    # exact multiples must not round up
+    assert O.keep_count(5, 16000) == 800
+    assert O.keep_count(20, 96) == 20       # 19.2 -> 20
+    assert O.keep_count(5, 49152) == 2458   # 2457.6 -> 2458
+    assert O.keep_count(0, 10) == 0 and O.keep_count(100, 10) == 10
+    assert O.keep_count(1, 1) == 1
+    with pytest.raises(ValueError):
+        O.keep_count(101, 5)
+
+
+# ------------------------------------------------------------------------------ LayerNorm
+def test_layernorm_closed_forms():
+    # constant row -> 0
+    assert np.all(O.layernorm(np.full((1, 9), 3.25)) == 0.0)
+    # [1,2,3,4]: mean 2.5, biased variance 1.25
+    y = O.layernorm(np.array([[1.0, 2.0, 3.0, 4.0]]))
+    expect = (np.array([1, 2, 3, 4]) - 2.5) / math.sqrt(1.25 + 1e-5)
+    assert np.allclose(y, expect, rtol=0, atol=1e-15)
+    # mean 0 and variance sigma^2 / (sigma^2 + eps) on random rows
+    x = np.random.default_rng(0).normal(3.0, 0.01, size=(5, 64))
+    y = O.layernorm(x)
+    var = x.var(axis=1)
+    assert np.allclose(y.mean(axis=1), 0.0, atol=1e-12)
+    assert np.allclose(y.var(axis=1), var / (var + 1e-5), rtol=1e-12)
+
+
+def test_layernorm_matches_torch_float64():
+    x = np.random.default_rng(1).normal(size=(3, 50))
+    ref = torch.nn.functional.layer_norm(torch.from_numpy(x), (50,), eps=1e-5).numpy()
+    assert np.allclose(O.layernorm(x), ref, rtol=1e-13, atol=1e-13)
+
+
+# ------------------------------------------------------------------------------ predictor
+def test_predictor_brute_force_loops():
+    rng = np.random.default_rng(2)
+    B, d, r, n = 2, 5, 3, 4
+    y, P1, P2 = rng.normal(size=(B, d)), rng.normal(size=(r, d)), rng.normal(size=(n, r))
+    z = O.predictor_logits_f64(y, P1, P2)
+    for b in range(B):
+        u = [max(0.0, sum(P1[c][j] * y[b][j] for j in range(d))) for c in range(r)]
+        for o in range(n):
+            assert abs(z[b, o] - sum(P2[o][c] * u[c] for c in range(r))) < 1e-12
+    assert O.predictor_logits(y, P1, P2).dtype == np.float32
+
+
+def test_predictor_closed_form():
+    # P1 = identity (r = d) and P2 = one row of ones: z = sum of the positive parts of y
+    y = np.array([[1.5, -2.0, 0.25, 4.0]])
+    z = O.predictor_logits_f64(y, np.eye(4), np.ones((1, 4)))
+    assert z[0, 0] == 5.75
+    # the hidden ReLU matters: a negative hidden unit contributes nothing
+    z = O.predictor_logits_f64(np.array([[1.0, 1.0]]), np.array([[1.0, 0.0], [-1.0, 0.0]]),
+                               np.array([[1.0, 10.0]]))
+    assert z[0, 0] == 1.0
+
+
+# ------------------------------------------------------------------------------ selection
+def test_select_golden_fixture():
+    g = _load("select_tiny.json")
+    z = np.array([_num(v) for v in g["z"]], dtype=np.float32)
+    for k, expect in g["topk"].items():
+        assert O.topk_set(z, int(k)).tolist() == expect, k
+    for t, expect in g["threshold"].items():
+        assert O.threshold_set(z, float(t)).tolist() == expect, t
+
+
+def _beats(z, i, j):
+    """i ranks strictly above j under (score desc, index asc), NaN = -inf, -0 = +0."""
+    zi = -math.inf if math.isnan(z[i]) else z[i] + 0.0
+    zj = -math.inf if math.isnan(z[j]) else z[j] + 0.0
+    return zi > zj or (zi == zj and i < j)
+
+
+@pytest.mark.parametrize("alphabet", [(0.0, 1.0), (0.0, 1.0, 2.0), (-0.0, 0.0, 1.0),
+                                      (math.nan, -math.inf, 1.0), (2.0, 2.0 + 2 ** -22, 3.0, -1.0)])
+def test_topk_exhaustive_tie_patterns(alphabet):
+    a = np.array(alphabet, dtype=np.float32)
+    for n in range(1, 7):
+        for combo in itertools.product(range(len(a)), repeat=n):
+            z = a[list(combo)]
+            for k in range(n + 1):
+                S = O.topk_set(z, k)
+                assert len(S) == k and list(S) == sorted(S)
+                rest = [j for j in range(n) if j not in set(S.tolist())]
+                assert all(_beats(z, i, j) for i in S for j in rest)
+                # the valid set is unique: brute force over all k-subsets
+                if n <= 5:
+                    valid = [c for c in itertools.combinations(range(n), k)
+                             if all(_beats(z, i, j) for i in c for j in range(n) if j not in c)]
+                    assert valid == [tuple(S.tolist())]
+
+
+def test_threshold_is_sigmoid_rule():
+    z = np.random.default_rng(4).normal(scale=3.0, size=500).astype(np.float32)
+    for t in (0.5, 0.1, 0.3, 0.77, 0.95):
+        tau = float(O.logit_threshold(t))
+        keep = [j for j in range(len(z)) if abs(float(z[j]) - tau) > 1e-6]
+        by_sigmoid = {j for j in keep if 1.0 / (1.0 + math.exp(-float(z[j]))) > float(np.float32(t))}
+        got = set(O.threshold_set(z, t).tolist())
+        assert by_sigmoid == {j for j in got if j in set(keep)}
+    assert O.threshold_set(z, 0.5).tolist() == np.flatnonzero(z > 0).tolist()
+    with pytest.raises(ValueError):
+        O.threshold_set(z, 1.0)
+
+
+def test_union_over_batch():
+    z = synth.make_scores(4, 37, seed=9).numpy()
+    for k in (0, 1, 5, 37):
+        U = O.select(z, O.TOPK, k=k)
+        sets = [set(O.topk_set(row, k).tolist()) for row in z]
+        assert set(U.tolist()) == set().union(*sets)
+        assert list(U) == sorted(U) and len(U) <= min(37, 4 * k)
+    assert O.select(z[:1], O.TOPK, k=5).tolist() == O.topk_set(z[0], 5).tolist()
+
+
+# ------------------------------------------------------------------------------ MLP
+def test_mlp_golden_fixture():
+    g = _load("mlp_tiny.json")
+    y, W1, b1, W2 = (_arr(g[k]) for k in ("y", "W1", "b1", "W2"))
+    for c in g["cases"]:
+        assert np.array_equal(O.sparse_mlp(y, W1, b1, W2, c["S_M"]), np.array(c["out"]))
+    assert np.array_equal(O.dense_mlp(y, W1, b1, W2), np.array(g["cases"][0]["out"]))
+
+
+def test_mlp_brute_force_loops_and_masked_dense():
+    s, L, P, x = _tiny(B=2)
+    y = O.layernorm(x)
+    S = [1, 4, 5, 17, 39]
+    got = O.sparse_mlp(y, L.W1, L.b1, L.W2, S)
+    W1, b1, W2 = (np.asarray(a, np.float64) for a in (L.W1, L.b1, L.W2))
+    for b in range(s.B):
+        out = [0.0] * s.d
+        for j in S:
+            a = max(0.0, sum(W1[j][c] * y[b][c] for c in range(s.d)) + b1[j])
+            for c in range(s.d):
+                out[c] += a * W2[j][c]
+        assert _rel(got[b], out) < 1e-13
+    # masked dense: activations outside S zeroed
+    mask = np.zeros(s.N)
+    mask[S] = 1.0
+    hidden = np.maximum(0.0, y @ W1.T + b1) * mask
+    assert _rel(got, hidden @ W2) < 1e-13
+    # S = all neurons is the dense MLP
+    assert _rel(O.sparse_mlp(y, L.W1, L.b1, L.W2, np.arange(s.N)), O.dense_mlp(y, L.W1, L.b1, L.W2)) < 1e-13
+    # a single neuron: a_j * W2[j]
+    j = 17
+    a = np.maximum(0.0, y @ W1[j] + b1[j])
+    assert _rel(O.sparse_mlp(y, L.W1, L.b1, L.W2, [j]), a[:, None] * W2[j][None, :]) < 1e-14
+
+
+def test_mlp_neuron_permutation_equivariance():
+    s, L, P, x = _tiny()
+    y = O.layernorm(x)
+    perm = np.random.default_rng(5).permutation(s.N)
+    inv = np.argsort(perm)
+    S = np.array([0, 3, 9, 33])
+    a = O.sparse_mlp(y, L.W1, L.b1, L.W2, S)
+    b = O.sparse_mlp(y, L.W1[perm], L.b1[perm], L.W2[perm], np.sort(inv[S]))
+    assert _rel(a, b) < 1e-13
+
+
+# ------------------------------------------------------------------------------ attention
+def _attn_fixture():
+    g = _load("attention_tiny.json")
+    Wqkv = _arr(g["Wqkv"]).reshape(g["h"], 3, g["dh"], g["d"])
+    return g, _arr(g["y"]), Wqkv, _arr(g["Wo"]), _arr(g["K"]), _arr(g["V"])
+
+
+def test_attention_golden_fixture():
+    g, y, Wqkv, Wo, K, V = _attn_fixture()
+    for c in g["cases"]:
+        out, _, _ = O.sparse_mha(y, Wqkv, Wo, K, V, g["n"], c["S_A"], g["scale"])
+        assert np.allclose(out, np.array(c["out"]), rtol=1e-14, atol=1e-14), c
+    dense, _, _ = O.dense_mha(y, Wqkv, Wo, K, V, g["n"], g["scale"])
+    assert np.allclose(dense, np.array(g["cases"][0]["out"]), rtol=1e-14, atol=1e-14)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_attention_all_heads_is_dense(dtype):
+    s, L, P, x = _tiny(B=2, dtype=dtype)
+    y = O.layernorm(x)
+    sp, kn, vn = O.sparse_mha(y, L.Wqkv, L.Wo, L.K, L.V, s.n, np.arange(s.h), 0.4)
+    de, kd, vd = O.dense_mha(y, L.Wqkv, L.Wo, L.K, L.V, s.n, 0.4)
+    assert _rel(sp, de) < 1e-13
+    assert np.array_equal(kn, kd) and np.array_equal(vn, vd)
+    assert kn.dtype == L.K.dtype
+
+
+def test_attention_empty_cache_returns_rounded_value():
+    # n = 0: the token attends to itself only, so H_i = rne(v_i) and the output is
+    # rne(v_i) W_i^O.
+    s, L, P, x = _tiny(dtype="f16")
+    y = O.layernorm(x)
+    i = 2
+    out, kn, vn = O.sparse_mha(y, L.Wqkv, L.Wo, L.K, L.V, 0, [i], 1.0)
+    v = np.asarray(L.Wqkv[i, 2], np.float64) @ y[0]
+    assert np.array_equal(vn[0, 0], v.astype(np.float16))
+    expect = vn[0, 0].astype(np.float64) @ np.asarray(L.Wo[i * s.dh:(i + 1) * s.dh], np.float64)
+    assert _rel(out[0], expect) < 1e-14
+
+
+def test_attention_equal_keys_average_values_and_hull():
+    s, L, P, x = _tiny()
+    y = O.layernorm(x)
+    Wqkv = L.Wqkv.copy()
+    Wqkv[:, 1] = 0.0                       # new key = 0
+    K = np.zeros_like(L.K)                 # cached keys = 0: all scores equal
+    for i in range(s.h):
+        _, _, vn = O.sparse_mha(y, Wqkv, L.Wo, K, L.V, s.n, [i], 1.0)
+        vals = np.concatenate([L.V[0, i, :s.n].astype(np.float64), vn[0, 0][None].astype(np.float64)])
+        H = vals.mean(axis=0)
+        out, _, _ = O.sparse_mha(y, Wqkv, L.Wo, K, L.V, s.n, [i], 1.0)
+        assert _rel(out[0], H @ L.Wo[i * s.dh:(i + 1) * s.dh].astype(np.float64)) < 1e-13
+    # general keys: H lies inside the per-column hull of the values; probe it with an
+    # identity output projection on one head
+    Wo = np.zeros((s.h * s.dh, s.d))
+    Wo[:s.dh, :s.dh] = np.eye(s.dh)
+    out, _, vn = O.sparse_mha(y, L.Wqkv, Wo, L.K, L.V, s.n, [0], 0.7)
+    vals = np.concatenate([L.V[0, 0, :s.n].astype(np.float64), vn[0, 0][None].astype(np.float64)])
+    H = out[0, :s.dh]
+    assert np.all(H >= vals.min(axis=0) - 1e-12) and np.all(H <= vals.max(axis=0) + 1e-12)
+
+
+def test_attention_sharp_softmax_selects_best_key():
+    # scale large: the softmax becomes one-hot on the key with the largest score
+    _, y, Wqkv, Wo, K, V = _attn_fixture()
+    out, _, _ = O.sparse_mha(y, Wqkv, Wo, K, V, 2, [0], 60.0)
+    assert np.allclose(out, [[5.0, -5.0]], rtol=1e-12)   # head 0's new key ln3 wins -> value 5
+    # scores far beyond exp's range: the normalisation must still give the one-hot result
+    out, _, _ = O.sparse_mha(y, Wqkv, Wo, K, V, 2, [0], 1.0e4)
+    assert np.array_equal(out, [[5.0, -5.0]])
+
+
+def test_attention_heads_add():
+    s, L, P, x = _tiny()
+    y = O.layernorm(x)
+    full, _, _ = O.sparse_mha(y, L.Wqkv, L.Wo, L.K, L.V, s.n, [0, 2, 3], 0.5)
+    parts = sum(O.sparse_mha(y, L.Wqkv, L.Wo, L.K, L.V, s.n, [i], 0.5)[0] for i in (0, 2, 3))
+    assert _rel(full, parts) < 1e-14
+
+
+def test_attention_brute_force_loops():
+    s, L, P, x = _tiny(d=8, h=2, dh=3, n=4)
+    y = O.layernorm(x)
+    scale = 0.6
+    out, kn, vn = O.sparse_mha(y, L.Wqkv, L.Wo, L.K, L.V, s.n, [1], scale)
+    W = np.asarray(L.Wqkv, np.float64)
+    i = 1
+    q = [sum(W[i, 0, c, j] * y[0, j] for j in range(s.d)) for c in range(s.dh)]
+    k = [float(np.float32(sum(W[i, 1, c, j] * y[0, j] for j in range(s.d)))) for c in range(s.dh)]
+    v = [float(np.float32(sum(W[i, 2, c, j] * y[0, j] for j in range(s.d)))) for c in range(s.dh)]
+    keys = [list(map(float, L.K[0, i, t])) for t in range(s.n)] + [k]
+    vals = [list(map(float, L.V[0, i, t])) for t in range(s.n)] + [v]
+    sc = [scale * sum(q[c] * kk[c] for c in range(s.dh)) for kk in keys]
+    w = [math.exp(e) for e in sc]
+    H = [sum(w[t] * vals[t][c] for t in range(len(w))) / sum(w) for c in range(s.dh)]
+    Wo = np.asarray(L.Wo, np.float64)
+    expect = [sum(H[c] * Wo[i * s.dh + c, j] for c in range(s.dh)) for j in range(s.d)]
+    assert _rel(out[0], expect) < 1e-13
+
+
+# ------------------------------------------------------------------------------ layer / stack
+def test_layer_all_sets_is_dense_layer():
+    s, L, P, x = _tiny(B=2)
+    sp, sp1, _, _ = O.sparse_layer(x, L, np.arange(s.h), np.arange(s.N), s.n, 0.3)
+    de, de1 = O.dense_layer(x, L, s.n, 0.3)
+    assert _rel(sp1, de1) < 1e-13 and _rel(sp, de) < 1e-13
+
+
+def test_layer_residual_structure():
+    s, L, P, x = _tiny()
+    Z = O.LayerWeights(L.Wqkv, np.zeros_like(L.Wo), L.W1, L.b1, np.zeros_like(L.W2), L.K, L.V)
+    out, x1, _, _ = O.sparse_layer(x, Z, [0, 1], [2, 3], s.n, 0.3)
+    assert np.array_equal(out, x.astype(np.float64)) and np.array_equal(x1, x.astype(np.float64))
+    # attention alone: x' = x + MHA(LN(x)), and the MLP reads LN(x')
+    out, x1, _, _ = O.sparse_layer(x, L, [0, 1], [2, 3], s.n, 0.3)
+    att, _, _ = O.sparse_mha(O.layernorm(x), L.Wqkv, L.Wo, L.K, L.V, s.n, [0, 1], 0.3)
+    assert _rel(x1, x + att) < 1e-15
+    assert _rel(out, x1 + O.sparse_mlp(O.layernorm(x1), L.W1, L.b1, L.W2, [2, 3])) < 1e-15
+
+
+def test_serial_layer_predicts_from_block_inputs():
+    s, L, P, x = _tiny()
+    sel = O.Selection(O.TOPK, k_A=2, k_M=6)
+    out, x1, S_A, S_M, _, _ = O.serial_layer(x, L, P, sel, s.n, 0.3)
+    assert S_A.tolist() == O.topk_set(O.predictor_logits(O.layernorm(x), P.P1_A, P.P2_A)[0], 2).tolist()
+    assert S_M.tolist() == O.topk_set(O.predictor_logits(O.layernorm(x1), P.P1_M, P.P2_M)[0], 6).tolist()
+    assert _rel(out, O.sparse_layer(x, L, S_A, S_M, s.n, 0.3)[0]) < 1e-15
+
+
+def test_lookahead_schedule():
+    shapes = []
+    layers, preds = [], []
+    for l in range(3):
+        s = synth.LayerShape(d=24, N=40, h=4, dh=6, n=7, r=10, dtype="f32")
+        layers.append(O.LayerWeights(**{k: v.numpy() for k, v in synth.make_layer(s, 11, l).items()}))
+        preds.append(O.PredictorWeights(**{k: v.numpy() for k, v in synth.make_predictors(s, 11, l).items()}))
+        shapes.append(s)
+    x0 = synth.make_input(shapes[0], 11).numpy()
+    sel = O.Selection(O.TOPK, k_A=1, k_M=4)
+    xL, xs, sets = O.lookahead_stack(x0, layers, preds, sel, 7, 0.4)
+    # layer 0 serially from LN(x_0); layer l+1 from LN(x_l), the input of layer l
+    for l in range(3):
+        src = xs[max(l - 1, 0)]
+        S_A, S_M = O.predict_sets(O.layernorm(src), preds[l], sel)
+        assert sets[l][0].tolist() == S_A.tolist() and sets[l][1].tolist() == S_M.tolist()
+        assert _rel(xs[l + 1], O.sparse_layer(xs[l], layers[l], *sets[l], 7, 0.4)[0]) < 1e-15
+    assert xL is xs[-1]

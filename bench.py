@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Sparse decode-step benchmark on one MI355X.
+
+A step is one decode token through a stack of OPT-175B-shaped layers (d 12288, 49152
+neurons, 96 heads of 128, 2048 cached positions, predictor width 1024, fp16 weights,
+batch 1): per layer LayerNorm, the two sparsity predictors and top-k selection (5% of
+neurons, 20% of heads; layer l+1's sets predicted on a second stream while layer l
+runs), head-sparse Q/K/V with the KV append, attention over the kept heads, the
+head-sparse output projection, LayerNorm, and the sparse MLP.  Every layer has its own
+weights and cache, all resident in HBM before timing starts.
+
+Prints one JSON line: HBM GB/s on the bytes the step touches (the value), microseconds
+per layer, the dense path on the same stack, the roofline of the dominant kernel
+(head-sparse Q/K/V GEMV) measured with HIP events around its launches, and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
+
+
+def parse(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="opt175b-24layers-fp16")
+    ap.add_argument("--layers", type=int, default=0, help="override the layer count (0: the workload's)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--dense-steps", type=int, default=3)
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget")
+    ap.add_argument("--breakdown", action="store_true", help="time every kernel family")
+    ap.add_argument("--no-lookahead", action="store_true")
+    return ap.parse_args(argv)
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------------ algorithmic bytes
+def layer_bytes(s, k_A, k_M):
+    """Bytes one sparse layer must touch (weights of the kept units, predictors, the kept
+    heads' KV rows); activations are a few KiB and left out."""
+    e = 2 if s.dtype == "f16" else 4
+    pred = (2 * s.d * s.r + s.r * s.N + s.r * s.h) * e
+    qkv = 3 * s.d * s.dh * k_A * e
+    o = k_A * s.dh * s.d * e
+    kv = s.B * 2 * (s.n + 1) * s.dh * k_A * e
+    mlp = 2 * k_M * s.d * e + k_M * e
+    return {"pred": pred, "qkv": qkv, "o_proj": o, "kv": kv, "mlp": mlp,
+            "total": pred + qkv + o + kv + mlp}
+
+
+def dense_layer_bytes(s):
+    e = 2 if s.dtype == "f16" else 4
+    return 4 * s.d * s.h * s.dh * e + 2 * s.N * s.d * e + s.N * e + s.B * 2 * (s.n + 1) * s.h * s.dh * e
+
+
+# ------------------------------------------------------------------------ CPU oracle baseline
+def cpu_baseline(wl, s, layers_gpu, preds_gpu, x0, k_A, k_M, budget_s, lb):
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    host = lambda t: t.detach().cpu().numpy()
+    sel = O.Selection(O.TOPK, k_A=k_A, k_M=k_M)
+    x = host(x0).astype(np.float64)
+    done, t_total = 0, 0.0
+    prev_y = None
+    for l in range(len(layers_gpu)):
+        w, p = layers_gpu[l], preds_gpu[l]
+        Lw = O.LayerWeights(**{k: host(v) for k, v in w.items()})
+        Pw = O.PredictorWeights(**{k: host(v) for k, v in p.items()})
+        t0 = time.perf_counter()
+        # one layer of the lookahead stack: the sets of layer l come from LN(x_{l-1})
+        y_src = O.layernorm(x) if prev_y is None else prev_y
+        S_A, S_M = O.predict_sets(y_src, Pw, sel)
+        prev_y = O.layernorm(x)
+        x, _, _, _ = O.sparse_layer(x, Lw, S_A, S_M, s.n, wl.scale)
+        t_total += time.perf_counter() - t0
+        done += 1
+        del Lw, Pw
+        if t_total >= budget_s:
+            break
+    per_layer_s = t_total / done
+    return {
+        "value": round(lb / per_layer_s / 1e9, 4), "unit": "GB/s",
+        "us_per_layer": round(per_layer_s * 1e6, 1),
+        "cores": int(threads), "host_cpus": os.cpu_count(), "kind": "oracle",
+        "sample": f"first {done} of {len(layers_gpu)} layers of one decode step (float64 numpy "
+                  f"oracle, lookahead sets), {t_total:.1f} s of CPU work",
+    }
+
+
+def main(argv=None) -> int:
+    args = parse(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        return 2
+    import torch
+    from contextual_sparsity_amd import configs, synth
+    from contextual_sparsity_amd import dejavu as dj
+
+    wl = configs.WORKLOADS[args.workload]
+    s = wl.shape
+    L = args.layers or wl.layers
+    k_A, k_M = wl.k_A, wl.k_M
+    dev = "cuda"
+    log(f"{dj.dejavu_version()}  device {torch.cuda.get_device_name(0)}  workload {wl.name} L={L}")
+
+    # ---- seeded weights, all resident before timing
+    t0 = time.time()
+    layers, preds = [], []
+    for l in range(L):
+        layers.append(synth.make_layer(s, args.seed, l, dev))
+        preds.append(synth.make_predictors(s, args.seed, l, dev))
+        if l % 4 == 3 or l == L - 1:
+            torch.cuda.synchronize()
+            log(f"generated layer {l + 1}/{L} ({time.time() - t0:.1f} s, "
+                f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB)")
+    x0 = synth.make_input(s, args.seed, dev)
+    wt = dj.DJV_F16 if s.dtype == "f16" else dj.DJV_F32
+    m = dj.make_model(wt, s.B, s.d, s.N, s.h, s.dh, s.r, s.n, s.cap, wl.scale, dj.DJV_TOPK, k_A, k_M)
+    desc = [dj.make_layer(layers[l], preds[l]) for l in range(L)]
+    ws = dj.workspace(dj.dejavu_workspace_bytes_model(m), dev)
+    x = x0.clone()
+    s_main = torch.cuda.current_stream()
+    s_pred = torch.cuda.Stream()
+    lookahead = not args.no_lookahead
+
+    def step(dense=False):
+        x.copy_(x0)
+        dj.dejavu_stack_decode(m, desc, x, lookahead, dense, None, ws, s_main, s_pred)
+
+    def timed(n, dense=False):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        a.record(s_main)
+        for _ in range(n):
+            step(dense)
+        b.record(s_main)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n, (time.perf_counter() - w0) * 1e3 / n
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("warm-up done")
+    ms_step, wall_ms = timed(args.steps)
+    log(f"sparse step {ms_step:.3f} ms (wall {wall_ms:.3f} ms)")
+    lb = layer_bytes(s, k_A, k_M)
+    step_bytes = lb["total"] * L
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+
+    # ---- dominant kernel: head-sparse Q/K/V GEMV, events around each of its launches
+    def family_time(fam, n_steps):
+        cap = n_steps * L + 4
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * cap)]
+        dj.dejavu_profile_kernel(fam, evs)
+        for _ in range(n_steps):
+            step()
+        used = dj.dejavu_profile_count()
+        torch.cuda.synchronize()
+        dj.dejavu_profile_kernel("off")
+        d = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(used)]
+        return sum(d) / max(1, len(d)), used
+
+    qkv_ms, qkv_n = family_time("qkv", args.steps)
+    qkv_bytes = lb["qkv"]
+    qkv_gbs = qkv_bytes / (qkv_ms * 1e-3) / 1e9
+    log(f"qkv GEMV {qkv_ms * 1e3:.1f} us/launch over {qkv_n} launches -> {qkv_gbs:.0f} GB/s")
+    kernels = {}
+    if args.breakdown:
+        fam_bytes = {"qkv": lb["qkv"], "mlp_up": k_M * s.d * (2 if s.dtype == "f16" else 4),
+                     "mlp_down": k_M * s.d * (2 if s.dtype == "f16" else 4), "o_proj": lb["o_proj"],
+                     "attn": lb["kv"], "pred_1": s.r * s.d * (2 if s.dtype == "f16" else 4),
+                     "pred_2": None, "select": None}
+        for fam in ("qkv", "mlp_up", "mlp_down", "o_proj", "attn", "pred_1", "pred_2", "select"):
+            ms_f, n_f = family_time(fam, max(3, args.steps // 4))
+            ent = {"us": round(ms_f * 1e3, 2), "launches": n_f}
+            if fam_bytes.get(fam):
+                ent["GBps"] = round(fam_bytes[fam] / (ms_f * 1e-3) / 1e9, 1)
+            kernels[fam] = ent
+            log(f"  {fam:9s} {ms_f * 1e3:8.1f} us  {ent.get('GBps', '')}")
+
+    # ---- dense path on the same stack
+    dense = None
+    if not args.no_dense:
+        step(dense=True)
+        torch.cuda.synchronize()
+        ms_dense, _ = timed(args.dense_steps, dense=True)
+        db = dense_layer_bytes(s) * L
+        dense = {"ms_per_step": round(ms_dense, 3), "us_per_layer": round(ms_dense * 1e3 / L, 2),
+                 "GBps": round(db / (ms_dense * 1e-3) / 1e9, 1),
+                 "pct_of_peak": round(100 * db / (ms_dense * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                 "bytes_per_layer": dense_layer_bytes(s)}
+        log(f"dense step {ms_dense:.3f} ms")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("CPU oracle sample ...")
+        cpu = cpu_baseline(wl, s, layers, preds, x0, k_A, k_M, args.cpu_seconds, lb["total"])
+        log(f"CPU oracle {cpu['us_per_layer']} us/layer on {cpu['cores']} threads")
+
+    out = {
+        "metric": "sparse decode-layer µs and HBM GB/s (% of peak), OPT-175B shape, 5% MLP/20% heads",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if s.dtype == "f16" else "f32",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,0.05) predictors, N(0,1) input)",
+        "config": {"workload": wl.name, "layers": L, "d": s.d, "N": s.N, "h": s.h, "dh": s.dh,
+                   "n": s.n, "r": s.r, "batch": s.B, "keep_neurons_pct": wl.pct_M,
+                   "keep_heads_pct": wl.pct_A, "k_M": k_M, "k_A": k_A, "lookahead": lookahead},
+        "us_per_layer": round(ms_step * 1e3 / L, 2),
+        "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(1e3 / ms_step, 1),
+        "bytes_per_layer": lb,
+        "wall_ms_per_step": round(wall_ms, 4),
+        "dense": dense,
+        "speedup_vs_dense": round(dense["ms_per_step"] / ms_step, 3) if dense else None,
+        "roofline": {"kernel": "head-sparse Q/K/V GEMV (gemv_kernel, QKV epilogue)", "bound": "hbm",
+                     "achieved": round(qkv_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(qkv_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": qkv_bytes, "us_per_launch": round(qkv_ms * 1e3, 2),
+                     "launches": qkv_n},
+        "kernels": kernels or None,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,707 @@
+// C ABI of libdejavu: argument validation, workspace layout and kernel sequencing.
+//
+// Every entry point validates all of its arguments before the first HIP call, so each
+// error path can be exercised on a machine without a GPU.  Kernels are enqueued on the
+// caller's stream; nothing here allocates device memory or synchronises (except
+// dejavu_poll_device_error).
+#include "dejavu.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "common.hpp"
+
+using namespace djv;
+
+namespace {
+
+thread_local std::string g_err;
+
+djv_status fail(djv_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+#define DJV_REQUIRE(cond, status, ...)                 \
+    do {                                               \
+        if (!(cond)) return fail(status, __VA_ARGS__); \
+    } while (0)
+
+#define DJV_TRY(expr)                                  \
+    do {                                               \
+        djv_status s_ = (expr);                        \
+        if (s_ != DJV_OK) return s_;                   \
+    } while (0)
+
+#define DJV_HIP(expr)                                                                      \
+    do {                                                                                   \
+        hipError_t e_ = (expr);                                                            \
+        if (e_ != hipSuccess) return fail(DJV_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+    } while (0)
+
+constexpr int kMaxSelect = 65536;
+constexpr int kMaxRowBytes = 256 * 8 * 16;  // one row: 256 threads x 8 vectors of 16 bytes
+
+size_t esize(int wt) { return wt == DJV_F16 ? 2 : 4; }
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+int words_of(int n) { return (n + 31) / 32; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+djv_status check_dtype(int wt) {
+    DJV_REQUIRE(wt == DJV_F32 || wt == DJV_F16, DJV_EINVAL, "dtype must be DJV_F32 or DJV_F16 (got %d)", wt);
+    return DJV_OK;
+}
+djv_status check_batch(int B) {
+    DJV_REQUIRE(B >= 1, DJV_EINVAL, "B must be >= 1 (got %d)", B);
+    DJV_REQUIRE(B <= DJV_MAX_BATCH, DJV_EUNSUPPORTED, "B = %d exceeds this build's limit %d", B, DJV_MAX_BATCH);
+    return DJV_OK;
+}
+djv_status check_rowlen(int cols, int wt, const char* name) {
+    DJV_REQUIRE(cols > 0, DJV_EINVAL, "%s must be > 0 (got %d)", name, cols);
+    DJV_REQUIRE(cols % 8 == 0, DJV_EINVAL, "%s must be a multiple of 8 (got %d)", name, cols);
+    DJV_REQUIRE((size_t)cols * esize(wt) <= (size_t)kMaxRowBytes, DJV_EUNSUPPORTED,
+                "%s = %d: rows above %d bytes are not supported", name, cols, kMaxRowBytes);
+    return DJV_OK;
+}
+djv_status check_ptr(const void* p, const char* name) {
+    DJV_REQUIRE(p != nullptr, DJV_EINVAL, "%s is NULL", name);
+    DJV_REQUIRE(aligned(p, 16), DJV_EALIGN, "%s is not 16-byte aligned", name);
+    return DJV_OK;
+}
+djv_status check_opt_ptr(const void* p, const char* name) {
+    if (!p) return DJV_OK;
+    DJV_REQUIRE(aligned(p, 16), DJV_EALIGN, "%s is not 16-byte aligned", name);
+    return DJV_OK;
+}
+djv_status check_idx_ptr(const void* p, const char* name) {
+    DJV_REQUIRE(p != nullptr, DJV_EINVAL, "%s is NULL", name);
+    DJV_REQUIRE(aligned(p, 4), DJV_EALIGN, "%s is not 4-byte aligned", name);
+    return DJV_OK;
+}
+djv_status check_select(int n_out, int mode, int k, float t, const char* what) {
+    DJV_REQUIRE(n_out >= 1, DJV_EINVAL, "%s: n_out must be >= 1 (got %d)", what, n_out);
+    DJV_REQUIRE(n_out <= kMaxSelect, DJV_EUNSUPPORTED, "%s: n_out = %d exceeds %d", what, n_out, kMaxSelect);
+    DJV_REQUIRE(mode == DJV_TOPK || mode == DJV_THRESHOLD, DJV_EINVAL, "%s: unknown mode %d", what, mode);
+    if (mode == DJV_TOPK)
+        DJV_REQUIRE(k >= 0 && k <= n_out, DJV_EINVAL, "%s: k = %d outside [0, %d]", what, k, n_out);
+    else
+        DJV_REQUIRE(t > 0.f && t < 1.f, DJV_EINVAL, "%s: t must lie in (0, 1)", what);
+    return DJV_OK;
+}
+djv_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
+    if (need == 0) return DJV_OK;
+    DJV_REQUIRE(ws != nullptr, DJV_EINVAL, "workspace is NULL (%zu bytes needed)", need);
+    DJV_REQUIRE(aligned(ws, 256), DJV_EALIGN, "workspace is not 256-byte aligned");
+    DJV_REQUIRE(ws_bytes >= need, DJV_EWORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+    return DJV_OK;
+}
+
+// Order-preserving key of an fp32 score (same map as the selection kernel).
+uint32_t score_key_host(float z) {
+    uint32_t u;
+    std::memcpy(&u, &z, 4);
+    if (z != z) u = 0xFF800000u;
+    if ((u & 0x7FFFFFFFu) == 0u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+uint32_t tau_key(float t) {
+    const double td = (double)t;
+    const float tau = (float)std::log(td / (1.0 - td));
+    return score_key_host(tau);
+}
+
+// ------------------------------------------------------------------------------------
+// Workspace plans.  The same functions size the workspace (base == nullptr) and carve
+// it, so a size query and a call always agree.
+// ------------------------------------------------------------------------------------
+struct Arena {
+    char* base;
+    size_t off = 0;
+    explicit Arena(void* b) : base(static_cast<char*>(b)) {}
+    template <typename T> T* take(size_t n) {
+        T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+        off += al256(n * sizeof(T));
+        return p;
+    }
+};
+
+struct PredWs { float* u; float* z; uint32_t* bits; };
+PredWs plan_predict(Arena& A, int B, int r, int n_out, bool need_z) {
+    PredWs w;
+    w.u = A.take<float>((size_t)B * r);
+    w.z = need_z ? A.take<float>((size_t)B * n_out) : nullptr;
+    w.bits = A.take<uint32_t>((size_t)B * words_of(n_out));
+    return w;
+}
+
+struct MlpWs { float* a; float* partial; int rpc; };
+MlpWs plan_mlp(Arena& A, int B, int d, int cap, bool f16) {
+    MlpWs w;
+    w.a = A.take<float>((size_t)B * cap);
+    const int nch = axpy_chunks(cap, d, f16, &w.rpc);
+    w.partial = A.take<float>((size_t)nch * B * d);
+    return w;
+}
+
+struct MhaWs { float* q; float* part; float* H; float* partial; int rpc, chunk, nchunk_max; };
+MhaWs plan_mha(Arena& A, int B, int d, int dh, int cap, int n_cap, bool f16) {
+    MhaWs w;
+    w.chunk = attn_chunk_for(f16, dh);
+    w.nchunk_max = (n_cap + w.chunk - 1) / w.chunk;
+    w.q = A.take<float>((size_t)B * cap * dh);
+    w.part = A.take<float>((size_t)B * cap * w.nchunk_max * (dh + 2));
+    w.H = A.take<float>((size_t)B * cap * dh);
+    const int nch = axpy_chunks(cap * dh, d, f16, &w.rpc);
+    w.partial = A.take<float>((size_t)nch * B * d);
+    return w;
+}
+
+int cap_of(int mode, int k, int n) { return mode == DJV_TOPK ? k : n; }
+
+struct LayerWs {
+    float* y[2];          // block inputs (ring of two for the lookahead schedule)
+    float* xa;            // x' = x + attention
+    float* y2;            // LN(x')
+    int32_t* idxA[2]; int32_t* cntA[2];
+    int32_t* idxM[2]; int32_t* cntM[2];
+    MhaWs mha; MlpWs mlp;             // main-stream scratch
+    PredWs predA, predM;              // predictor-stream scratch
+};
+LayerWs plan_layer(Arena& A, const djv_model& m) {
+    const bool f16 = m.wt == DJV_F16;
+    LayerWs w;
+    for (int i = 0; i < 2; ++i) w.y[i] = A.take<float>((size_t)m.B * m.d);
+    w.xa = A.take<float>((size_t)m.B * m.d);
+    w.y2 = A.take<float>((size_t)m.B * m.d);
+    for (int i = 0; i < 2; ++i) {
+        w.idxA[i] = A.take<int32_t>(m.h);
+        w.cntA[i] = A.take<int32_t>(1);
+        w.idxM[i] = A.take<int32_t>(m.N);
+        w.cntM[i] = A.take<int32_t>(1);
+    }
+    w.mha = plan_mha(A, m.B, m.d, m.dh, cap_of(m.mode, m.k_A, m.h), m.n_cap, f16);
+    w.mlp = plan_mlp(A, m.B, m.d, cap_of(m.mode, m.k_M, m.N), f16);
+    w.predA = plan_predict(A, m.B, m.r, m.h, true);
+    w.predM = plan_predict(A, m.B, m.r, m.N, true);
+    return w;
+}
+
+// Dense-path scratch: all heads and all neurons.
+struct DenseWs { float* y; float* xa; float* y2; MhaWs mha; MlpWs mlp; };
+DenseWs plan_dense(Arena& A, const djv_model& m) {
+    const bool f16 = m.wt == DJV_F16;
+    DenseWs w;
+    w.y = A.take<float>((size_t)m.B * m.d);
+    w.xa = A.take<float>((size_t)m.B * m.d);
+    w.y2 = A.take<float>((size_t)m.B * m.d);
+    w.mha = plan_mha(A, m.B, m.d, m.dh, m.h, m.n_cap, f16);
+    w.mlp = plan_mlp(A, m.B, m.d, m.N, f16);
+    return w;
+}
+
+// ------------------------------------------------------------------------------------
+// Kernel sequences shared by the entry points (arguments already validated)
+// ------------------------------------------------------------------------------------
+djv_status run_predict(bool f16, int B, int d, int r, int n_out, const float* y, const void* P1,
+                       const void* P2, int mode, int k, float t, int32_t* idx, int32_t* count,
+                       float* z, const PredWs& w, hipStream_t s) {
+    unsigned* flags = device_flags();
+    GemvArgs g{};
+    g.W = P1; g.cols = d; g.list = UnitList{nullptr, nullptr, r, r}; g.rpu = 1;
+    g.y = y; g.B = B; g.epi = kEpiRelu; g.out = w.u; g.ld = r; g.flags = flags;
+    g.prof = DJV_PROF_PRED_1;
+    DJV_HIP(launch_gemv(f16, g, s));
+    g = GemvArgs{};
+    g.W = P2; g.cols = r; g.list = UnitList{nullptr, nullptr, n_out, n_out}; g.rpu = 1;
+    g.y = w.u; g.B = B; g.epi = kEpiStore; g.out = z; g.ld = n_out; g.flags = flags;
+    g.prof = DJV_PROF_PRED_2;
+    DJV_HIP(launch_gemv(f16, g, s));
+    SelectJob j{z, n_out, mode, k, mode == DJV_THRESHOLD ? tau_key(t) : 0u, w.bits, idx, count};
+    DJV_HIP(launch_select(&j, 1, B, s, DJV_PROF_SELECT));
+    return DJV_OK;
+}
+
+djv_status run_mlp(bool f16, int B, int d, int N, const float* y, const void* W1, const void* b1,
+                   const void* W2, const int32_t* idx, const int32_t* count, int cap,
+                   const float* resid, float* out, const MlpWs& w, hipStream_t s) {
+    unsigned* flags = device_flags();
+    const UnitList list{idx, count, cap, N};
+    GemvArgs g{};
+    g.W = W1; g.cols = d; g.list = list; g.rpu = 1; g.y = y; g.B = B; g.epi = kEpiBiasRelu;
+    g.out = w.a; g.ld = cap; g.bias = b1; g.flags = flags; g.prof = DJV_PROF_MLP_UP;
+    DJV_HIP(launch_gemv(f16, g, s));
+    AxpyArgs x{};
+    x.W = W2; x.cols = d; x.list = list; x.rpu = 1; x.coef = w.a; x.ldc = cap; x.B = B;
+    x.partial = w.partial; x.rows_per_chunk = w.rpc; x.resid = resid; x.out = out; x.flags = flags;
+    x.prof = DJV_PROF_MLP_DOWN;
+    DJV_HIP(launch_axpy(f16, x, s));
+    return DJV_OK;
+}
+
+djv_status run_mha(bool f16, int B, int d, int h, int dh, int n, int n_cap, const float* y,
+                   const void* Wqkv, const void* Wo, void* Kc, void* Vc, const int32_t* idx,
+                   const int32_t* count, int cap, float scale, const float* resid, float* out,
+                   const MhaWs& w, hipStream_t s) {
+    unsigned* flags = device_flags();
+    const UnitList list{idx, count, cap, h};
+    GemvArgs g{};
+    g.W = Wqkv; g.cols = d; g.list = list; g.rpu = 3 * dh; g.y = y; g.B = B; g.epi = kEpiQkv;
+    g.out = w.q; g.ld = cap * dh; g.Kc = Kc; g.Vc = Vc; g.h = h; g.dh = dh; g.n = n;
+    g.n_cap = n_cap; g.flags = flags; g.prof = DJV_PROF_QKV;
+    DJV_HIP(launch_gemv(f16, g, s));
+    AttnArgs at{};
+    at.Kc = Kc; at.Vc = Vc; at.list = list; at.h = h; at.dh = dh; at.n = n; at.n_cap = n_cap;
+    at.B = B; at.q = w.q; at.scale = scale; at.part = w.part; at.chunk = w.chunk;
+    at.nchunk = (n + 1 + w.chunk - 1) / w.chunk; at.H = w.H; at.flags = flags;
+    at.prof = DJV_PROF_ATTN;
+    DJV_HIP(launch_attention(f16, at, s));
+    AxpyArgs x{};
+    x.W = Wo; x.cols = d; x.list = list; x.rpu = dh; x.coef = w.H; x.ldc = cap * dh; x.B = B;
+    x.partial = w.partial; x.rows_per_chunk = w.rpc; x.resid = resid; x.out = out; x.flags = flags;
+    x.prof = DJV_PROF_O_PROJ;
+    DJV_HIP(launch_axpy(f16, x, s));
+    return DJV_OK;
+}
+
+djv_status check_model(const djv_model* m) {
+    DJV_REQUIRE(m != nullptr, DJV_EINVAL, "model is NULL");
+    DJV_TRY(check_dtype(m->wt));
+    DJV_TRY(check_batch(m->B));
+    DJV_TRY(check_rowlen(m->d, m->wt, "d"));
+    DJV_TRY(check_rowlen(m->r, m->wt, "r"));
+    DJV_REQUIRE(m->N >= 1 && m->h >= 1, DJV_EINVAL, "N and h must be >= 1");
+    DJV_REQUIRE(m->dh == 64 || m->dh == 128, DJV_EUNSUPPORTED, "dh must be 64 or 128 (got %d)", m->dh);
+    DJV_REQUIRE(m->n >= 0 && m->n < m->n_cap, DJV_EINVAL, "need 0 <= n < n_cap (n = %d, n_cap = %d)", m->n, m->n_cap);
+    DJV_REQUIRE(std::isfinite(m->scale), DJV_EINVAL, "scale must be finite");
+    DJV_REQUIRE(m->eps > 0.f && std::isfinite(m->eps), DJV_EINVAL, "eps must be > 0");
+    DJV_TRY(check_select(m->h, m->mode, m->k_A, m->t_A, "head selection"));
+    DJV_TRY(check_select(m->N, m->mode, m->k_M, m->t_M, "neuron selection"));
+    return DJV_OK;
+}
+
+djv_status check_layer(const djv_layer* L, bool dense) {
+    DJV_REQUIRE(L != nullptr, DJV_EINVAL, "layer descriptor is NULL");
+    DJV_TRY(check_ptr(L->Wqkv, "Wqkv"));
+    DJV_TRY(check_ptr(L->Wo, "Wo"));
+    DJV_TRY(check_ptr(L->W1, "W1"));
+    DJV_REQUIRE(L->b1 != nullptr, DJV_EINVAL, "b1 is NULL");
+    DJV_TRY(check_ptr(L->W2, "W2"));
+    DJV_TRY(check_ptr(L->Kc, "Kc"));
+    DJV_TRY(check_ptr(L->Vc, "Vc"));
+    if (!dense) {
+        DJV_TRY(check_ptr(L->P1_A, "P1_A"));
+        DJV_TRY(check_ptr(L->P2_A, "P2_A"));
+        DJV_TRY(check_ptr(L->P1_M, "P1_M"));
+        DJV_TRY(check_ptr(L->P2_M, "P2_M"));
+    }
+    return DJV_OK;
+}
+
+size_t layer_ws_bytes(const djv_model& m) {
+    Arena A(nullptr);
+    plan_layer(A, m);
+    size_t s = A.off;
+    Arena D(nullptr);
+    plan_dense(D, m);
+    return s > D.off ? s : D.off;
+}
+
+djv_status copy_async(void* dst, const void* src, size_t bytes, hipStream_t s) {
+    if (!dst || bytes == 0) return DJV_OK;
+    DJV_HIP(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s));
+    return DJV_OK;
+}
+
+// Copies a layer's sets into the optional trace.
+djv_status trace_sets(const djv_trace* tr, const djv_model& m, int l, const LayerWs& w, int buf,
+                      hipStream_t s) {
+    if (!tr) return DJV_OK;
+    const int capA = cap_of(m.mode, m.k_A, m.h), capM = cap_of(m.mode, m.k_M, m.N);
+    if (tr->sets_A) DJV_TRY(copy_async(tr->sets_A + (size_t)l * m.h, w.idxA[buf], capA * 4, s));
+    if (tr->sets_M) DJV_TRY(copy_async(tr->sets_M + (size_t)l * m.N, w.idxM[buf], capM * 4, s));
+    if (tr->counts) {
+        DJV_TRY(copy_async(tr->counts + 2 * l, w.cntA[buf], 4, s));
+        DJV_TRY(copy_async(tr->counts + 2 * l + 1, w.cntM[buf], 4, s));
+    }
+    return DJV_OK;
+}
+
+djv_status trace_x(const djv_trace* tr, const djv_model& m, int l, const float* x, hipStream_t s) {
+    if (!tr || !tr->x_in) return DJV_OK;
+    return copy_async(tr->x_in + (size_t)l * m.B * m.d, x, (size_t)m.B * m.d * 4, s);
+}
+
+// Score buffers of layer l: the trace's when it asks for them, else the workspace's.
+float* zA_of(const djv_trace* tr, const djv_model& m, int l, const LayerWs& w) {
+    return (tr && tr->z_A) ? tr->z_A + (size_t)l * m.B * m.h : w.predA.z;
+}
+float* zM_of(const djv_trace* tr, const djv_model& m, int l, const LayerWs& w) {
+    return (tr && tr->z_M) ? tr->z_M + (size_t)l * m.B * m.N : w.predM.z;
+}
+
+// Predicts the head set of layer l from y into buffer `buf`.
+djv_status predict_A(const djv_model& m, const djv_layer& L, const float* y, const LayerWs& w,
+                     int buf, const djv_trace* tr, int l, hipStream_t s) {
+    return run_predict(m.wt == DJV_F16, m.B, m.d, m.r, m.h, y, L.P1_A, L.P2_A, m.mode, m.k_A,
+                       m.t_A, w.idxA[buf], w.cntA[buf], zA_of(tr, m, l, w), w.predA, s);
+}
+// Predicts the neuron set of layer l from y into buffer `buf`.
+djv_status predict_M(const djv_model& m, const djv_layer& L, const float* y, const LayerWs& w,
+                     int buf, const djv_trace* tr, int l, hipStream_t s) {
+    return run_predict(m.wt == DJV_F16, m.B, m.d, m.r, m.N, y, L.P1_M, L.P2_M, m.mode, m.k_M,
+                       m.t_M, w.idxM[buf], w.cntM[buf], zM_of(tr, m, l, w), w.predM, s);
+}
+
+// Attention then MLP of layer l with the sets in buffer `buf`; y = LN(x) given.  With
+// predict_M_here the neuron set is predicted from LN(x') in between (serial schedule).
+djv_status layer_body(const djv_model& m, const djv_layer& L, float* x, const float* y,
+                      const LayerWs& w, int buf, bool predict_M_here, const djv_trace* tr, int l,
+                      hipStream_t s) {
+    const bool f16 = m.wt == DJV_F16;
+    DJV_TRY(run_mha(f16, m.B, m.d, m.h, m.dh, m.n, m.n_cap, y, L.Wqkv, L.Wo, L.Kc, L.Vc,
+                    w.idxA[buf], w.cntA[buf], cap_of(m.mode, m.k_A, m.h), m.scale, x, w.xa,
+                    w.mha, s));
+    if (tr && tr->x_mid)
+        DJV_TRY(copy_async(tr->x_mid + (size_t)l * m.B * m.d, w.xa, (size_t)m.B * m.d * 4, s));
+    DJV_HIP(launch_layernorm(m.B, m.d, w.xa, w.y2, m.eps, s));
+    if (predict_M_here) DJV_TRY(predict_M(m, L, w.y2, w, buf, tr, l, s));
+    DJV_TRY(run_mlp(f16, m.B, m.d, m.N, w.y2, L.W1, L.b1, L.W2, w.idxM[buf], w.cntM[buf],
+                    cap_of(m.mode, m.k_M, m.N), w.xa, x, w.mlp, s));
+    return DJV_OK;
+}
+
+}  // namespace
+
+// ======================================================================================
+// Entry points
+// ======================================================================================
+extern "C" {
+
+const char* dejavu_last_error(void) { return g_err.c_str(); }
+
+const char* dejavu_version(void) { return "dejavu-mi355x 0.1 (gfx950)"; }
+
+djv_status dejavu_workspace_bytes(int B, int d, int N, int h, int dh, int r, int n_cap,
+                                  size_t* bytes) {
+    DJV_REQUIRE(bytes != nullptr, DJV_EINVAL, "bytes is NULL");
+    DJV_REQUIRE(B >= 0 && d >= 0 && N >= 0 && h >= 0 && dh >= 0 && r >= 0 && n_cap >= 0,
+                DJV_EINVAL, "sizes must be >= 0");
+    const int Bq = B > 0 ? B : 1;
+    size_t need = 0;
+    auto upd = [&](size_t v) { if (v > need) need = v; };
+    for (int f = 0; f < 2; ++f) {
+        const bool f16 = f == 1;
+        const int n_out = N > h ? N : h;
+        if (n_out > 0) {
+            Arena a(nullptr);
+            plan_predict(a, Bq, r, n_out, true);
+            upd(a.off);
+        }
+        if (N > 0 && d > 0) {
+            Arena a(nullptr);
+            plan_mlp(a, Bq, d, N, f16);
+            upd(a.off);
+        }
+        if (h > 0 && d > 0 && dh > 0) {
+            Arena a(nullptr);
+            plan_mha(a, Bq, d, dh, h, n_cap > 0 ? n_cap : 1, f16);
+            upd(a.off);
+        }
+        if (N > 0 && h > 0 && d > 0 && dh > 0) {
+            djv_model m{};
+            m.wt = f16 ? DJV_F16 : DJV_F32; m.B = Bq; m.d = d; m.N = N; m.h = h; m.dh = dh;
+            m.r = r; m.n_cap = n_cap > 0 ? n_cap : 1; m.mode = DJV_THRESHOLD;
+            upd(layer_ws_bytes(m));
+        }
+    }
+    *bytes = need;
+    return DJV_OK;
+}
+
+djv_status dejavu_workspace_bytes_model(const djv_model* m, size_t* bytes) {
+    DJV_REQUIRE(bytes != nullptr, DJV_EINVAL, "bytes is NULL");
+    DJV_TRY(check_model(m));
+    *bytes = layer_ws_bytes(*m);
+    return DJV_OK;
+}
+
+djv_status dejavu_layernorm(int B, int d, const float* x, float* y, float eps, void* stream) {
+    DJV_REQUIRE(B >= 1 && d >= 1, DJV_EINVAL, "B and d must be >= 1");
+    DJV_REQUIRE(eps > 0.f && std::isfinite(eps), DJV_EINVAL, "eps must be > 0");
+    DJV_TRY(check_ptr(x, "x"));
+    DJV_TRY(check_ptr(y, "y"));
+    DJV_HIP(launch_layernorm(B, d, x, y, eps, (hipStream_t)stream));
+    return DJV_OK;
+}
+
+djv_status dejavu_select(int B, int n_out, const float* z, djv_mode mode, int k, float t,
+                         int32_t* idx, int32_t* count, void* ws, size_t ws_bytes, void* stream) {
+    DJV_REQUIRE(B >= 1 && B <= 65535, DJV_EINVAL, "B must lie in [1, 65535] (got %d)", B);
+    DJV_TRY(check_select(n_out, mode, k, t, "select"));
+    DJV_TRY(check_ptr(z, "z"));
+    DJV_TRY(check_idx_ptr(idx, "idx"));
+    DJV_TRY(check_idx_ptr(count, "count"));
+    Arena sz(nullptr);
+    sz.take<uint32_t>((size_t)B * words_of(n_out));
+    DJV_TRY(check_ws(ws, ws_bytes, sz.off));
+    Arena A(ws);
+    uint32_t* bits = A.take<uint32_t>((size_t)B * words_of(n_out));
+    SelectJob j{z, n_out, (int)mode, k, mode == DJV_THRESHOLD ? tau_key(t) : 0u, bits, idx, count};
+    DJV_HIP(launch_select(&j, 1, B, (hipStream_t)stream, DJV_PROF_SELECT));
+    return DJV_OK;
+}
+
+djv_status dejavu_predict(djv_dtype wt, int B, int d, int r, int n_out, const float* y,
+                          const void* P1, const void* P2, djv_mode mode, int k, float t,
+                          int32_t* idx, int32_t* count, float* logits,
+                          void* ws, size_t ws_bytes, void* stream) {
+    DJV_TRY(check_dtype(wt));
+    DJV_TRY(check_batch(B));
+    DJV_TRY(check_rowlen(d, wt, "d"));
+    DJV_TRY(check_rowlen(r, wt, "r"));
+    DJV_TRY(check_select(n_out, mode, k, t, "predict"));
+    DJV_TRY(check_ptr(y, "y"));
+    DJV_TRY(check_ptr(P1, "P1"));
+    DJV_TRY(check_ptr(P2, "P2"));
+    DJV_TRY(check_idx_ptr(idx, "idx"));
+    DJV_TRY(check_idx_ptr(count, "count"));
+    DJV_TRY(check_opt_ptr(logits, "logits"));
+    Arena sz(nullptr);
+    plan_predict(sz, B, r, n_out, logits == nullptr);
+    DJV_TRY(check_ws(ws, ws_bytes, sz.off));
+    Arena A(ws);
+    PredWs w = plan_predict(A, B, r, n_out, logits == nullptr);
+    float* z = logits ? logits : w.z;
+    return run_predict(wt == DJV_F16, B, d, r, n_out, y, P1, P2, mode, k, t, idx, count, z, w,
+                       (hipStream_t)stream);
+}
+
+static djv_status mlp_common(djv_dtype wt, int B, int d, int N, const float* y, const void* W1,
+                             const void* b1, const void* W2, const int32_t* idx,
+                             const int32_t* count, int cap, const float* resid, float* out,
+                             void* ws, size_t ws_bytes, void* stream) {
+    DJV_TRY(check_dtype(wt));
+    DJV_TRY(check_batch(B));
+    DJV_TRY(check_rowlen(d, wt, "d"));
+    DJV_REQUIRE(N >= 1, DJV_EINVAL, "N must be >= 1");
+    DJV_REQUIRE(cap >= 1 && cap <= N, DJV_EINVAL, "cap = %d outside [1, N = %d]", cap, N);
+    DJV_TRY(check_ptr(y, "y"));
+    DJV_TRY(check_ptr(W1, "W1"));
+    DJV_REQUIRE(b1 != nullptr, DJV_EINVAL, "b1 is NULL");
+    DJV_TRY(check_ptr(W2, "W2"));
+    DJV_TRY(check_opt_ptr(resid, "resid"));
+    DJV_TRY(check_ptr(out, "out"));
+    const bool f16 = wt == DJV_F16;
+    Arena sz(nullptr);
+    plan_mlp(sz, B, d, cap, f16);
+    DJV_TRY(check_ws(ws, ws_bytes, sz.off));
+    Arena A(ws);
+    MlpWs w = plan_mlp(A, B, d, cap, f16);
+    return run_mlp(f16, B, d, N, y, W1, b1, W2, idx, count, cap, resid, out, w, (hipStream_t)stream);
+}
+
+djv_status dejavu_sparse_mlp(djv_dtype wt, int B, int d, int N, const float* y, const void* W1,
+                             const void* b1, const void* W2, const int32_t* idx,
+                             const int32_t* count, int cap, const float* resid, float* out,
+                             void* ws, size_t ws_bytes, void* stream) {
+    DJV_TRY(check_idx_ptr(idx, "idx"));
+    DJV_TRY(check_idx_ptr(count, "count"));
+    return mlp_common(wt, B, d, N, y, W1, b1, W2, idx, count, cap, resid, out, ws, ws_bytes, stream);
+}
+
+djv_status dejavu_dense_mlp(djv_dtype wt, int B, int d, int N, const float* y, const void* W1,
+                            const void* b1, const void* W2, const float* resid, float* out,
+                            void* ws, size_t ws_bytes, void* stream) {
+    return mlp_common(wt, B, d, N, y, W1, b1, W2, nullptr, nullptr, N, resid, out, ws, ws_bytes,
+                      stream);
+}
+
+static djv_status mha_common(djv_dtype wt, int B, int d, int h, int dh, int n, int n_cap,
+                             const float* y, const void* Wqkv, const void* Wo, void* Kc, void* Vc,
+                             const int32_t* idx, const int32_t* count, int cap, float scale,
+                             const float* resid, float* out, void* ws, size_t ws_bytes,
+                             void* stream) {
+    DJV_TRY(check_dtype(wt));
+    DJV_TRY(check_batch(B));
+    DJV_TRY(check_rowlen(d, wt, "d"));
+    DJV_REQUIRE(h >= 1, DJV_EINVAL, "h must be >= 1");
+    DJV_REQUIRE(dh == 64 || dh == 128, DJV_EUNSUPPORTED, "dh must be 64 or 128 (got %d)", dh);
+    DJV_REQUIRE(n >= 0 && n < n_cap, DJV_EINVAL, "need 0 <= n < n_cap (n = %d, n_cap = %d)", n, n_cap);
+    DJV_REQUIRE(cap >= 1 && cap <= h, DJV_EINVAL, "cap = %d outside [1, h = %d]", cap, h);
+    DJV_REQUIRE(std::isfinite(scale), DJV_EINVAL, "scale must be finite");
+    DJV_TRY(check_ptr(y, "y"));
+    DJV_TRY(check_ptr(Wqkv, "Wqkv"));
+    DJV_TRY(check_ptr(Wo, "Wo"));
+    DJV_TRY(check_ptr(Kc, "Kc"));
+    DJV_TRY(check_ptr(Vc, "Vc"));
+    DJV_TRY(check_opt_ptr(resid, "resid"));
+    DJV_TRY(check_ptr(out, "out"));
+    const bool f16 = wt == DJV_F16;
+    Arena sz(nullptr);
+    plan_mha(sz, B, d, dh, cap, n_cap, f16);
+    DJV_TRY(check_ws(ws, ws_bytes, sz.off));
+    Arena A(ws);
+    MhaWs w = plan_mha(A, B, d, dh, cap, n_cap, f16);
+    return run_mha(f16, B, d, h, dh, n, n_cap, y, Wqkv, Wo, Kc, Vc, idx, count, cap, scale, resid,
+                   out, w, (hipStream_t)stream);
+}
+
+djv_status dejavu_sparse_mha(djv_dtype wt, int B, int d, int h, int dh, int n, int n_cap,
+                             const float* y, const void* Wqkv, const void* Wo, void* Kc, void* Vc,
+                             const int32_t* head_idx, const int32_t* head_count, int cap,
+                             float scale, const float* resid, float* out, void* ws,
+                             size_t ws_bytes, void* stream) {
+    DJV_TRY(check_idx_ptr(head_idx, "head_idx"));
+    DJV_TRY(check_idx_ptr(head_count, "head_count"));
+    return mha_common(wt, B, d, h, dh, n, n_cap, y, Wqkv, Wo, Kc, Vc, head_idx, head_count, cap,
+                      scale, resid, out, ws, ws_bytes, stream);
+}
+
+djv_status dejavu_dense_mha(djv_dtype wt, int B, int d, int h, int dh, int n, int n_cap,
+                            const float* y, const void* Wqkv, const void* Wo, void* Kc, void* Vc,
+                            float scale, const float* resid, float* out, void* ws,
+                            size_t ws_bytes, void* stream) {
+    return mha_common(wt, B, d, h, dh, n, n_cap, y, Wqkv, Wo, Kc, Vc, nullptr, nullptr, h, scale,
+                      resid, out, ws, ws_bytes, stream);
+}
+
+djv_status dejavu_sparse_layer(const djv_model* m, const djv_layer* layer, float* x,
+                               const djv_trace* trace, void* ws, size_t ws_bytes, void* stream) {
+    DJV_TRY(check_model(m));
+    DJV_TRY(check_layer(layer, false));
+    DJV_TRY(check_ptr(x, "x"));
+    DJV_TRY(check_ws(ws, ws_bytes, layer_ws_bytes(*m)));
+    hipStream_t s = (hipStream_t)stream;
+    Arena A(ws);
+    const LayerWs w = plan_layer(A, *m);
+    DJV_TRY(trace_x(trace, *m, 0, x, s));
+    DJV_HIP(launch_layernorm(m->B, m->d, x, w.y[0], m->eps, s));
+    DJV_TRY(predict_A(*m, *layer, w.y[0], w, 0, trace, 0, s));
+    DJV_TRY(layer_body(*m, *layer, x, w.y[0], w, 0, true, trace, 0, s));
+    return trace_sets(trace, *m, 0, w, 0, s);
+}
+
+djv_status dejavu_stack_decode(const djv_model* m, const djv_layer* layers, int L, float* x,
+                               int lookahead, int dense, const djv_trace* trace, void* ws,
+                               size_t ws_bytes, void* s_main, void* s_pred) {
+    DJV_TRY(check_model(m));
+    DJV_REQUIRE(L >= 1, DJV_EINVAL, "L must be >= 1");
+    DJV_REQUIRE(layers != nullptr, DJV_EINVAL, "layers is NULL");
+    for (int l = 0; l < L; ++l) DJV_TRY(check_layer(&layers[l], dense != 0));
+    DJV_TRY(check_ptr(x, "x"));
+    DJV_TRY(check_ws(ws, ws_bytes, layer_ws_bytes(*m)));
+    hipStream_t sm = (hipStream_t)s_main, sp = (hipStream_t)s_pred;
+    const bool f16 = m->wt == DJV_F16;
+
+    if (dense) {
+        Arena A(ws);
+        const DenseWs w = plan_dense(A, *m);
+        for (int l = 0; l < L; ++l) {
+            const djv_layer& Ly = layers[l];
+            DJV_TRY(trace_x(trace, *m, l, x, sm));
+            DJV_HIP(launch_layernorm(m->B, m->d, x, w.y, m->eps, sm));
+            DJV_TRY(run_mha(f16, m->B, m->d, m->h, m->dh, m->n, m->n_cap, w.y, Ly.Wqkv, Ly.Wo,
+                            Ly.Kc, Ly.Vc, nullptr, nullptr, m->h, m->scale, x, w.xa, w.mha, sm));
+            DJV_HIP(launch_layernorm(m->B, m->d, w.xa, w.y2, m->eps, sm));
+            DJV_TRY(run_mlp(f16, m->B, m->d, m->N, w.y2, Ly.W1, Ly.b1, Ly.W2, nullptr, nullptr,
+                            m->N, w.xa, x, w.mlp, sm));
+        }
+        return DJV_OK;
+    }
+
+    Arena A(ws);
+    const LayerWs w = plan_layer(A, *m);
+    if (!lookahead) {
+        for (int l = 0; l < L; ++l) {
+            DJV_TRY(trace_x(trace, *m, l, x, sm));
+            DJV_HIP(launch_layernorm(m->B, m->d, x, w.y[0], m->eps, sm));
+            DJV_TRY(predict_A(*m, layers[l], w.y[0], w, 0, trace, l, sm));
+            DJV_TRY(layer_body(*m, layers[l], x, w.y[0], w, 0, true, trace, l, sm));
+            DJV_TRY(trace_sets(trace, *m, l, w, 0, sm));
+        }
+        return DJV_OK;
+    }
+
+    // Lookahead schedule: S^{l+1} from y_l on the predictor stream while layer l runs.
+    hipEvent_t evY = nullptr, evS = nullptr;
+    DJV_HIP(hipEventCreateWithFlags(&evY, hipEventDisableTiming));
+    if (hipEventCreateWithFlags(&evS, hipEventDisableTiming) != hipSuccess) {
+        (void)hipEventDestroy(evY);
+        return fail(DJV_EHIP, "hipEventCreateWithFlags failed");
+    }
+    struct Guard {
+        hipEvent_t a, b;
+        ~Guard() { (void)hipEventDestroy(a); (void)hipEventDestroy(b); }
+    } guard{evY, evS};
+
+    DJV_TRY(trace_x(trace, *m, 0, x, sm));
+    DJV_HIP(launch_layernorm(m->B, m->d, x, w.y[0], m->eps, sm));
+    DJV_TRY(predict_A(*m, layers[0], w.y[0], w, 0, trace, 0, sm));
+    DJV_TRY(predict_M(*m, layers[0], w.y[0], w, 0, trace, 0, sm));
+    DJV_HIP(hipEventRecord(evY, sm));
+    for (int l = 0; l < L; ++l) {
+        const int cur = l & 1, nxt = (l + 1) & 1;
+        if (l >= 1) DJV_HIP(hipStreamWaitEvent(sm, evS, 0));  // S^l ready
+        DJV_TRY(trace_sets(trace, *m, l, w, cur, sm));
+        if (l + 1 < L) {
+            DJV_HIP(hipStreamWaitEvent(sp, evY, 0));           // y_l ready, buffer nxt free
+            DJV_TRY(predict_A(*m, layers[l + 1], w.y[cur], w, nxt, trace, l + 1, sp));
+            DJV_TRY(predict_M(*m, layers[l + 1], w.y[cur], w, nxt, trace, l + 1, sp));
+            DJV_HIP(hipEventRecord(evS, sp));
+        }
+        DJV_TRY(layer_body(*m, layers[l], x, w.y[cur], w, cur, false, trace, l, sm));
+        if (l + 1 < L) {
+            DJV_TRY(trace_x(trace, *m, l + 1, x, sm));
+            DJV_HIP(launch_layernorm(m->B, m->d, x, w.y[nxt], m->eps, sm));
+            DJV_HIP(hipEventRecord(evY, sm));
+        }
+    }
+    return DJV_OK;
+}
+
+djv_status dejavu_profile_kernel(int family, void* const* events, int capacity) {
+    DJV_REQUIRE(family >= DJV_PROF_OFF && family <= DJV_PROF_SELECT, DJV_EINVAL,
+                "unknown kernel family %d", family);
+    ProfHook& h = prof_hook();
+    if (family == DJV_PROF_OFF) {
+        h = ProfHook{};
+        return DJV_OK;
+    }
+    DJV_REQUIRE(events != nullptr && capacity >= 1, DJV_EINVAL, "events and capacity >= 1 are required");
+    h.family = family;
+    h.ev = events;
+    h.cap = capacity;
+    h.used = 0;
+    h.open = false;
+    return DJV_OK;
+}
+
+djv_status dejavu_profile_count(int* count) {
+    DJV_REQUIRE(count != nullptr, DJV_EINVAL, "count is NULL");
+    *count = prof_hook().used;
+    return DJV_OK;
+}
+
+djv_status dejavu_poll_device_error(void* stream, uint32_t* flags) {
+    DJV_REQUIRE(flags != nullptr, DJV_EINVAL, "flags is NULL");
+    unsigned* dflags = device_flags();
+    DJV_REQUIRE(dflags != nullptr, DJV_EHIP, "device flag word unavailable");
+    DJV_HIP(hipStreamSynchronize((hipStream_t)stream));
+    unsigned v = 0;
+    DJV_HIP(hipMemcpy(&v, dflags, sizeof v, hipMemcpyDeviceToHost));
+    const unsigned zero = 0;
+    DJV_HIP(hipMemcpy(dflags, &zero, sizeof zero, hipMemcpyHostToDevice));
+    *flags = v;
+    return DJV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,245 @@
+// Shared device helpers and the internal launch interface of libdejavu.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace djv {
+
+constexpr int kWave = 64;          // CDNA wavefront width
+constexpr int kMaxBatch = 4;       // batch rows held in registers by the GEMV kernels
+constexpr unsigned kFlagBadIndex = 1u;
+constexpr unsigned kFlagBadCount = 2u;
+
+// ------------------------------------------------------------------------------------
+// 16-byte vector of weights and its conversion to fp32
+// ------------------------------------------------------------------------------------
+struct alignas(16) Vec16 {
+    uint32_t w[4];
+};
+
+template <typename T> struct WTraits;
+template <> struct WTraits<float> {
+    static constexpr int kPerVec = 4;   // elements per 16-byte vector
+};
+template <> struct WTraits<__half> {
+    static constexpr int kPerVec = 8;
+};
+
+__device__ __forceinline__ Vec16 ldg16(const void* p) {
+    // Plain global 128-bit load; weights are streamed once per call.
+    return *reinterpret_cast<const Vec16*>(p);
+}
+
+__device__ __forceinline__ Vec16 ldg16_nt(const void* p) {
+    // Non-temporal 128-bit load for streamed weights that are not reused.
+    Vec16 v;
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q));
+    v.w[0] = t[0]; v.w[1] = t[1]; v.w[2] = t[2]; v.w[3] = t[3];
+    return v;
+}
+
+__device__ __forceinline__ float lo_h(uint32_t u) {
+    return __half2float(__ushort_as_half((unsigned short)(u & 0xffffu)));
+}
+__device__ __forceinline__ float hi_h(uint32_t u) {
+    return __half2float(__ushort_as_half((unsigned short)(u >> 16)));
+}
+
+// Expand a vector into fp32 elements.
+template <typename T>
+__device__ __forceinline__ void unpack(const Vec16& v, float (&f)[WTraits<T>::kPerVec]);
+template <>
+__device__ __forceinline__ void unpack<float>(const Vec16& v, float (&f)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v.w[i]);
+}
+template <>
+__device__ __forceinline__ void unpack<__half>(const Vec16& v, float (&f)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = lo_h(v.w[i]);
+        f[2 * i + 1] = hi_h(v.w[i]);
+    }
+}
+
+// Round an fp32 value to the storage type (round-to-nearest-even).
+template <typename T> __device__ __forceinline__ T to_store(float x);
+template <> __device__ __forceinline__ float to_store<float>(float x) { return x; }
+template <> __device__ __forceinline__ __half to_store<__half>(float x) { return __float2half_rn(x); }
+
+template <typename T> __device__ __forceinline__ float to_f32(T x);
+template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ float to_f32<__half>(__half x) { return __half2float(x); }
+
+// ------------------------------------------------------------------------------------
+// Reductions
+// ------------------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+__device__ __forceinline__ void set_flag(unsigned* flags, unsigned bit) {
+    if (flags) atomicOr(flags, bit);
+}
+
+// ------------------------------------------------------------------------------------
+// Row maps: which weight rows a launch visits.
+//   A unit (a neuron, a head, a predictor output) owns `rpu` consecutive rows.
+//   Unit slot u in [0, count) names unit idx[u] (or u when idx == nullptr).
+// ------------------------------------------------------------------------------------
+struct UnitList {
+    const int32_t* idx;    // ascending unit indices (nullptr: identity)
+    const int32_t* count;  // device count (nullptr: cap)
+    int cap;               // list capacity
+    int units;             // number of units in the weight tensor
+};
+
+__device__ __forceinline__ int read_count(const UnitList& L, unsigned* flags) {
+    if (!L.count) return L.cap;
+    int c = *L.count;
+    if (c < 0 || c > L.cap) {
+        set_flag(flags, kFlagBadCount);
+        c = c < 0 ? 0 : L.cap;
+    }
+    return c;
+}
+
+// Returns the unit of slot u or -1 (and flags it) when the index is out of range.
+__device__ __forceinline__ int unit_of(const UnitList& L, int u, unsigned* flags) {
+    if (!L.idx) return u;
+    int j = L.idx[u];
+    if (j < 0 || j >= L.units) {
+        set_flag(flags, kFlagBadIndex);
+        return -1;
+    }
+    return j;
+}
+
+}  // namespace djv
+
+// ------------------------------------------------------------------------------------
+// Internal launchers (defined in the kernel translation units)
+// ------------------------------------------------------------------------------------
+namespace djv {
+
+enum GemvEpi : int {
+    kEpiStore = 0,      // out[b*ld + r] = acc
+    kEpiRelu = 1,       // out[b*ld + r] = max(acc, 0)
+    kEpiBiasRelu = 2,   // out[b*ld + u] = max(acc + bias[unit], 0)
+    kEpiQkv = 3,        // q -> out, k/v -> cache position n (rounded to the cache dtype)
+};
+
+struct GemvArgs {
+    const void* W;        // weights, rows of `cols` elements
+    int cols;             // row length in elements (d or r)
+    UnitList list;        // which units
+    int rpu;              // rows per unit
+    const float* y;       // [B, cols] fp32
+    int B;
+    int epi;
+    float* out;           // fp32 output
+    int ld;               // leading dimension of out per batch row
+    const void* bias;     // kEpiBiasRelu: per-unit bias (weight dtype)
+    // kEpiQkv: cache [B, h, n_cap, dh]
+    void* Kc;
+    void* Vc;
+    int h, dh, n, n_cap;
+    unsigned* flags;
+    int prof;             // profiling family of this launch (0: none)
+};
+
+hipError_t launch_gemv(bool f16, const GemvArgs& a, hipStream_t s);
+
+struct AxpyArgs {
+    const void* W;        // [units*rpu, cols] weights
+    int cols;
+    UnitList list;
+    int rpu;
+    const float* coef;    // [B, ldc] fp32: coefficient of visited row r of batch b at b*ldc + r
+    int ldc;
+    int B;
+    float* partial;       // [nchunk, B, cols] workspace
+    int rows_per_chunk;
+    const float* resid;   // may be nullptr
+    float* out;           // [B, cols]
+    unsigned* flags;
+    int prof;
+};
+
+hipError_t launch_axpy(bool f16, const AxpyArgs& a, hipStream_t s);
+int axpy_chunks(int rows_cap, int cols, bool f16, int* rows_per_chunk);
+
+struct AttnArgs {
+    const void* Kc;       // [B, h, n_cap, dh]
+    const void* Vc;
+    UnitList list;        // heads
+    int h, dh, n, n_cap, B;
+    const float* q;       // [B, cap, dh]
+    float scale;
+    float* part;          // [B, cap, nchunk, dh + 2]
+    int chunk;            // positions per chunk
+    int nchunk;
+    float* H;             // [B, cap, dh]
+    unsigned* flags;
+    int prof;
+};
+
+hipError_t launch_attention(bool f16, const AttnArgs& a, hipStream_t s);
+int attn_chunk_for(bool f16, int dh);  // positions per attention chunk
+
+struct SelectJob {
+    const float* z;       // [B, n_out]
+    int n_out;
+    int mode;             // 0 top-k, 1 threshold
+    int k;
+    uint32_t tau_key;     // threshold in the order-preserving key space
+    uint32_t* bits;       // [B, words] per-row selection bitmaps (workspace)
+    int32_t* idx;         // [n_out]
+    int32_t* count;       // [1]
+};
+
+hipError_t launch_select(const SelectJob* jobs, int njobs, int B, hipStream_t s, int prof);
+
+hipError_t launch_layernorm(int B, int d, const float* x, float* y, float eps, hipStream_t s);
+
+unsigned* device_flags();  // this device's flag word (device address), nullptr on error
+
+// Benchmark hook: events recorded around the launches of one kernel family.
+struct ProfHook {
+    int family = 0;
+    void* const* ev = nullptr;  // 2 * cap hipEvent_t
+    int cap = 0;
+    int used = 0;
+    bool open = false;
+};
+ProfHook& prof_hook();
+
+inline void prof_begin(int family, hipStream_t s) {
+    ProfHook& h = prof_hook();
+    if (family != 0 && h.family == family && h.used < h.cap) {
+        (void)hipEventRecord(static_cast<hipEvent_t>(h.ev[2 * h.used]), s);
+        h.open = true;
+    }
+}
+inline void prof_end(int family, hipStream_t s) {
+    ProfHook& h = prof_hook();
+    if (h.open && h.family == family) {
+        (void)hipEventRecord(static_cast<hipEvent_t>(h.ev[2 * h.used + 1]), s);
+        ++h.used;
+        h.open = false;
+    }
+}
+
+}  // namespace djv

@@ -1,0 +1,68 @@
+"""Shared helpers for the GPU parity tests: seeded inputs on the device, host copies for
+the oracle, and the comparison rules."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import oracle as O
+from contextual_sparsity_amd import dejavu as dj
+from contextual_sparsity_amd import synth
+
+DEV = "cuda"
+
+# relative L2 tolerances by weight dtype (fp32 accumulation on the GPU)
+TOL = {"f32": 1e-5, "f16": 1e-2}
+
+
+def rel_l2(got, ref) -> float:
+    g = np.asarray(got, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(r)
+    return float(np.linalg.norm(g - r) / (den if den > 0 else 1.0))
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy()
+
+
+def wt_code(shape: synth.LayerShape) -> int:
+    return dj.DJV_F16 if shape.dtype == "f16" else dj.DJV_F32
+
+
+def ws_for(shape: synth.LayerShape) -> torch.Tensor:
+    n = dj.dejavu_workspace_bytes(shape.B, shape.d, shape.N, shape.h, shape.dh, shape.r, shape.cap)
+    return dj.workspace(n, DEV)
+
+
+def idx_tensor(S) -> tuple:
+    S = np.asarray(S, dtype=np.int32)
+    cap = max(1, len(S))
+    idx = torch.zeros(cap, dtype=torch.int32, device=DEV)
+    if len(S):
+        idx[:len(S)] = torch.from_numpy(S).to(DEV)
+    cnt = torch.tensor([len(S)], dtype=torch.int32, device=DEV)
+    return idx, cnt, cap
+
+
+def oracle_layer(w: dict) -> O.LayerWeights:
+    return O.LayerWeights(**{k: host(v) for k, v in w.items()})
+
+
+def oracle_preds(p: dict) -> O.PredictorWeights:
+    return O.PredictorWeights(**{k: host(v) for k, v in p.items()})
+
+
+def check_sets_valid(sel_gpu, z_oracle, k: int, delta: float) -> None:
+    """A top-k set chosen from slightly different scores is valid when every selected
+    oracle score is >= every unselected one minus 2*delta (delta = max score gap)."""
+    z = np.asarray(z_oracle, dtype=np.float64)
+    S = np.asarray(sel_gpu, dtype=np.int64)
+    assert len(S) == k and len(np.unique(S)) == k
+    if k == 0 or k == len(z):
+        return
+    mask = np.zeros(len(z), dtype=bool)
+    mask[S] = True
+    assert z[mask].min() >= z[~mask].max() - 2 * delta - 1e-30, (z[mask].min(), z[~mask].max(), delta)

@@ -1,0 +1,168 @@
+"""The C ABI on a host without a GPU: the library loads, exports every entry point the
+header declares, sizes workspaces, and rejects bad arguments with the documented status
+before making any HIP call (fake, never-dereferenced addresses are passed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from contextual_sparsity_amd import dejavu as dj
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dejavu.h")
+
+A = 0x10000000      # a 256-byte aligned fake device address (never dereferenced)
+MIS = A + 4         # misaligned
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:djv_status|const char\*)\s+(dejavu_\w+)\s*\(", src, re.M)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(dj.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = dj.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", dj.LIB_PATH], capture_output=True, text=True)
+    syms = set(re.findall(r"\sT\s+(dejavu_\w+)", out.stdout))
+    assert set(_declared()) <= syms
+    assert "gfx950" in dj.dejavu_version()
+
+
+def test_workspace_sizes():
+    small = dj.dejavu_workspace_bytes(1, 768, 3072, 12, 64, 128, 129)
+    big = dj.dejavu_workspace_bytes(1, 12288, 49152, 96, 128, 1024, 2049)
+    b4 = dj.dejavu_workspace_bytes(4, 12288, 49152, 96, 128, 1024, 2049)
+    assert 0 < small < big < b4
+    assert b4 < 64 << 20          # modest: tens of MiB at the OPT-175B shape
+    m = dj.make_model(dj.DJV_F16, 1, 12288, 49152, 96, 128, 1024, 2048, 2049, 128 ** -0.5,
+                      dj.DJV_TOPK, 20, 2458)
+    assert 0 < dj.dejavu_workspace_bytes_model(m) <= big
+    with pytest.raises(dj.DejavuError) as e:
+        dj.dejavu_workspace_bytes(-1)
+    assert e.value.status == dj.DJV_EINVAL
+
+
+def _status(fn, *args, **kw):
+    try:
+        fn(*args, **kw)
+    except dj.DejavuError as e:
+        assert dj.dejavu_last_error() == e.message and e.message
+        return e.status
+    return dj.DJV_OK
+
+
+WS = (A, 1 << 30)
+
+
+def test_select_argument_errors():
+    s = dj.dejavu_select
+    assert _status(s, 0, 10, A, dj.DJV_TOPK, 1, 0.5, A, A, WS) == dj.DJV_EINVAL
+    assert _status(s, 1, 0, A, dj.DJV_TOPK, 0, 0.5, A, A, WS) == dj.DJV_EINVAL
+    assert _status(s, 1, 70000, A, dj.DJV_TOPK, 1, 0.5, A, A, WS) == dj.DJV_EUNSUPPORTED
+    assert _status(s, 1, 10, A, dj.DJV_TOPK, 11, 0.5, A, A, WS) == dj.DJV_EINVAL
+    assert _status(s, 1, 10, A, dj.DJV_TOPK, -1, 0.5, A, A, WS) == dj.DJV_EINVAL
+    assert _status(s, 1, 10, A, dj.DJV_THRESHOLD, 0, 1.0, A, A, WS) == dj.DJV_EINVAL
+    assert _status(s, 1, 10, A, dj.DJV_THRESHOLD, 0, 0.0, A, A, WS) == dj.DJV_EINVAL
+    assert _status(s, 1, 10, A, 7, 0, 0.5, A, A, WS) == dj.DJV_EINVAL
+    assert _status(s, 1, 10, None, dj.DJV_TOPK, 1, 0.5, A, A, WS) == dj.DJV_EINVAL
+    assert _status(s, 1, 10, MIS, dj.DJV_TOPK, 1, 0.5, A, A, WS) == dj.DJV_EALIGN
+    assert _status(s, 1, 10, A, dj.DJV_TOPK, 1, 0.5, A, A + 2, WS) == dj.DJV_EALIGN
+    assert _status(s, 1, 10, A, dj.DJV_TOPK, 1, 0.5, A, A, (A, 0)) == dj.DJV_EWORKSPACE
+    assert _status(s, 1, 10, A, dj.DJV_TOPK, 1, 0.5, A, A, (A + 16, 1 << 20)) == dj.DJV_EALIGN
+    assert _status(s, 1, 10, A, dj.DJV_TOPK, 1, 0.5, A, A, None) == dj.DJV_EINVAL
+
+
+def test_predict_argument_errors():
+    p = dj.dejavu_predict
+    ok = dict(wt=dj.DJV_F16, B=1, d=768, r=128, n_out=3072, y=A, P1=A, P2=A, mode=dj.DJV_TOPK,
+              k=154, t=0.5, idx=A, count=A, logits=None, ws=WS)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return _status(p, **a)
+    assert call(wt=5) == dj.DJV_EINVAL
+    assert call(B=0) == dj.DJV_EINVAL
+    assert call(B=5) == dj.DJV_EUNSUPPORTED
+    assert call(d=100) == dj.DJV_EINVAL
+    assert call(d=20000) == dj.DJV_EUNSUPPORTED
+    assert call(r=0) == dj.DJV_EINVAL
+    assert call(k=3073) == dj.DJV_EINVAL
+    assert call(P2=None) == dj.DJV_EINVAL
+    assert call(P1=MIS) == dj.DJV_EALIGN
+    assert call(logits=MIS) == dj.DJV_EALIGN
+    assert call(ws=(A, 16)) == dj.DJV_EWORKSPACE
+
+
+def test_mlp_argument_errors():
+    f = dj.dejavu_sparse_mlp
+    ok = dict(wt=dj.DJV_F32, B=1, d=768, N=3072, y=A, W1=A, b1=A, W2=A, idx=A, count=A, cap=154,
+              resid=None, out=A, ws=WS)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return _status(f, **a)
+    assert call(cap=0) == dj.DJV_EINVAL
+    assert call(cap=3073) == dj.DJV_EINVAL
+    assert call(idx=None) == dj.DJV_EINVAL
+    assert call(count=A + 2) == dj.DJV_EALIGN
+    assert call(W2=MIS) == dj.DJV_EALIGN
+    assert call(resid=MIS) == dj.DJV_EALIGN
+    assert call(out=None) == dj.DJV_EINVAL
+    assert call(N=0) == dj.DJV_EINVAL
+    assert call(ws=(A, 1024)) == dj.DJV_EWORKSPACE
+    assert _status(dj.dejavu_dense_mlp, dj.DJV_F32, 1, 768, 3072, A, A, A, A, None, A, (A, 1024)) \
+        == dj.DJV_EWORKSPACE
+
+
+def test_mha_argument_errors():
+    f = dj.dejavu_sparse_mha
+    ok = dict(wt=dj.DJV_F16, B=1, d=768, h=12, dh=64, n=128, n_cap=129, y=A, Wqkv=A, Wo=A, Kc=A,
+              Vc=A, head_idx=A, head_count=A, cap=3, scale=0.125, resid=None, out=A, ws=WS)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return _status(f, **a)
+    assert call(dh=96) == dj.DJV_EUNSUPPORTED
+    assert call(n=129) == dj.DJV_EINVAL
+    assert call(n=-1) == dj.DJV_EINVAL
+    assert call(cap=13) == dj.DJV_EINVAL
+    assert call(scale=float("nan")) == dj.DJV_EINVAL
+    assert call(Kc=None) == dj.DJV_EINVAL
+    assert call(Vc=MIS) == dj.DJV_EALIGN
+    assert call(head_idx=None) == dj.DJV_EINVAL
+    assert call(ws=(A, 64)) == dj.DJV_EWORKSPACE
+
+
+def test_layer_and_stack_argument_errors():
+    m = dj.make_model(dj.DJV_F16, 1, 768, 3072, 12, 64, 128, 128, 129, 0.125, dj.DJV_TOPK, 3, 154)
+    w = {k: A for k in ("Wqkv", "Wo", "W1", "b1", "W2", "K", "V")}
+    p = {k: A for k in ("P1_A", "P2_A", "P1_M", "P2_M")}
+    L = dj.make_layer(w, p)
+    assert _status(dj.dejavu_sparse_layer, m, L, A, None, (A, 16)) == dj.DJV_EWORKSPACE
+    bad = dj.make_model(dj.DJV_F16, 1, 768, 3072, 12, 64, 128, 128, 129, 0.125, dj.DJV_TOPK, 13, 154)
+    assert _status(dj.dejavu_sparse_layer, bad, L, A, None, WS) == dj.DJV_EINVAL
+    bad = dj.make_model(dj.DJV_F16, 1, 768, 3072, 12, 64, 128, 128, 129, 0.125, dj.DJV_THRESHOLD, 0, 0,
+                        t_A=1.5)
+    assert _status(dj.dejavu_sparse_layer, bad, L, A, None, WS) == dj.DJV_EINVAL
+    bad = dj.make_model(dj.DJV_F16, 1, 768, 3072, 12, 64, 128, 128, 129, 0.125, eps=0.0)
+    assert _status(dj.dejavu_sparse_layer, bad, L, A, None, WS) == dj.DJV_EINVAL
+    L2 = dj.make_layer(w, dict(p, P2_M=None))
+    assert _status(dj.dejavu_sparse_layer, m, L2, A, None, WS) == dj.DJV_EINVAL
+    assert _status(dj.dejavu_stack_decode, m, [L, L2], A, True, False, None, WS) == dj.DJV_EINVAL
+    assert _status(dj.dejavu_stack_decode, m, [], A, True, False, None, WS) == dj.DJV_EINVAL
+    assert _status(dj.dejavu_layernorm, 1, 768, A, A, 0.0) == dj.DJV_EINVAL
+    assert _status(dj.dejavu_layernorm, 1, 768, MIS, A, 1e-5) == dj.DJV_EALIGN
+    with pytest.raises(dj.DejavuError):
+        dj.lib().dejavu_poll_device_error(None, None) and None or dj._check(
+            dj.lib().dejavu_poll_device_error(None, None))

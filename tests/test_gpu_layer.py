@@ -1,0 +1,197 @@
+"""Whole sparse layers and stacks on the GPU against the oracle, teacher-forced layer by
+layer: each layer's GPU input x and the GPU's selected sets are fed to the oracle.
+
+Checks per layer:
+  * the sets are exactly the oracle's selection on the GPU's own scores (bit-exact on
+    identical scores), the GPU scores match the oracle's scores of the same input, and
+    the sets are valid top-k sets of the oracle's scores within twice the score gap;
+  * x' (after attention) and the layer output match the oracle to the dtype tolerance.
+Also the full-size workloads: one OPT-125m layer (fp32), one OPT-175B-shaped layer,
+a 3-layer OPT-6.7B-shaped lookahead stack, one OPT-66B-shaped layer at batch 1 and 4."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from contextual_sparsity_amd import configs
+from contextual_sparsity_amd import dejavu as dj
+from contextual_sparsity_amd import synth
+from helpers import DEV, TOL, check_sets_valid, host, rel_l2, wt_code
+
+pytestmark = pytest.mark.gpu
+
+
+class Stack:
+    """Seeded weights of L layers on the device plus the library descriptors."""
+
+    def __init__(self, shape: synth.LayerShape, L: int, seed: int, k_A: int, k_M: int,
+                 mode=dj.DJV_TOPK, t_A=0.5, t_M=0.5):
+        self.s, self.L = shape, L
+        self.w = [synth.make_layer(shape, seed, l, DEV) for l in range(L)]
+        self.p = [synth.make_predictors(shape, seed, l, DEV) for l in range(L)]
+        self.x0 = synth.make_input(shape, seed, DEV)
+        self.k_A, self.k_M, self.mode, self.t_A, self.t_M = k_A, k_M, mode, t_A, t_M
+        self.scale = shape.dh ** -0.5
+        self.m = dj.make_model(wt_code(shape), shape.B, shape.d, shape.N, shape.h, shape.dh, shape.r,
+                               shape.n, shape.cap, self.scale, mode, k_A, k_M, t_A, t_M)
+        self.desc = [dj.make_layer(self.w[l], self.p[l]) for l in range(L)]
+        self.ws = dj.workspace(dj.dejavu_workspace_bytes_model(self.m), DEV)
+        # host copies of the caches before the step (the step appends at position n)
+        self.K0 = [host(w["K"]).copy() for w in self.w]
+        self.V0 = [host(w["V"]).copy() for w in self.w]
+
+    def trace(self):
+        s, L = self.s, self.L
+        f = lambda *shape: torch.zeros(*shape, dtype=torch.float32, device=DEV)
+        i = lambda *shape: torch.full(shape, -1, dtype=torch.int32, device=DEV)
+        t = dict(x_in=f(L, s.B, s.d), x_mid=f(L, s.B, s.d), z_A=f(L, s.B, s.h), z_M=f(L, s.B, s.N),
+                 sets_A=i(L, s.h), sets_M=i(L, s.N), counts=i(L, 2))
+        return t, dj.make_trace(**t)
+
+    def run(self, lookahead: bool, single_layer=False):
+        t, tr = self.trace()
+        x = self.x0.clone()
+        if single_layer:
+            dj.dejavu_sparse_layer(self.m, self.desc[0], x, tr, self.ws)
+        else:
+            s_pred = torch.cuda.Stream()
+            dj.dejavu_stack_decode(self.m, self.desc, x, lookahead, False, tr, self.ws,
+                                   torch.cuda.current_stream(), s_pred)
+        torch.cuda.synchronize()
+        return x, {k: host(v) for k, v in t.items()}
+
+
+def _rows(P, rows):
+    """Gather predictor / weight rows on the device before copying to the host."""
+    return host(P[torch.as_tensor(np.asarray(rows, dtype=np.int64), device=DEV)])
+
+
+def check_stack(st: Stack, x_out, tr, lookahead: bool, sel_k=True):
+    s, tol = st.s, TOL[st.s.dtype]
+    for l in range(st.L):
+        x_in, x_mid = tr["x_in"][l].astype(np.float64), tr["x_mid"][l].astype(np.float64)
+        cA, cM = int(tr["counts"][l, 0]), int(tr["counts"][l, 1])
+        S_A, S_M = tr["sets_A"][l, :cA], tr["sets_M"][l, :cM]
+        zA, zM = tr["z_A"][l], tr["z_M"][l]
+        # which input each predictor read
+        if lookahead:
+            src_A = src_M = tr["x_in"][max(l - 1, 0)]
+        else:
+            src_A, src_M = tr["x_in"][l], tr["x_mid"][l]
+        p = st.p[l]
+        zA_ref = O.predictor_logits_f64(O.layernorm(src_A), host(p["P1_A"]), host(p["P2_A"]))
+        zM_ref = O.predictor_logits_f64(O.layernorm(src_M), host(p["P1_M"]), host(p["P2_M"]))
+        assert rel_l2(zA, zA_ref) < tol and rel_l2(zM, zM_ref) < tol, l
+        # bit-exact selection on the GPU's own scores
+        assert np.array_equal(S_A, O.select(zA, st.mode, st.k_A, st.t_A)), l
+        assert np.array_equal(S_M, O.select(zM, st.mode, st.k_M, st.t_M)), l
+        if st.mode == dj.DJV_TOPK and s.B == 1:
+            check_sets_valid(S_A, zA_ref[0], st.k_A, float(np.abs(zA[0] - zA_ref[0]).max()))
+            check_sets_valid(S_M, zM_ref[0], st.k_M, float(np.abs(zM[0] - zM_ref[0]).max()))
+        # attention half from the GPU's input and head set
+        w = st.w[l]
+        Sa = np.asarray(S_A, dtype=np.int64)
+        ta = torch.as_tensor(Sa, device=DEV)
+        Wqkv = host(w["Wqkv"][ta])
+        Wo = host(w["Wo"].view(s.h, s.dh, s.d)[ta].reshape(-1, s.d))
+        K0, V0 = st.K0[l][:, Sa], st.V0[l][:, Sa]
+        att, kn, vn = O.sparse_mha(O.layernorm(x_in), Wqkv, Wo, K0, V0, s.n, np.arange(len(Sa)), st.scale)
+        assert rel_l2(x_mid - x_in, att) < tol, (l, rel_l2(x_mid - x_in, att))
+        # appended K/V rows of the selected heads
+        Kn = host(w["K"][:, ta, s.n])
+        assert rel_l2(Kn, kn) < tol, l
+        # MLP half from the GPU's x' and neuron set
+        Sm = np.asarray(S_M, dtype=np.int64)
+        tm = torch.as_tensor(Sm, device=DEV)
+        mlp = O.sparse_mlp(O.layernorm(x_mid), host(w["W1"][tm]), host(w["b1"][tm]), host(w["W2"][tm]),
+                           np.arange(len(Sm)))
+        x_next = x_out if l == st.L - 1 else tr["x_in"][l + 1]
+        assert rel_l2(np.asarray(x_next, np.float64) - x_mid, mlp) < tol, (l, rel_l2(x_next - x_mid, mlp))
+
+
+@pytest.mark.parametrize("dtype,B", [("f32", 1), ("f16", 1), ("f16", 3)])
+def test_serial_layer_small(dtype, B):
+    s = synth.LayerShape(d=1032, N=1500, h=6, dh=128 if dtype == "f16" else 64, n=300, r=136,
+                         dtype=dtype, B=B)
+    st = Stack(s, 1, 21, k_A=2, k_M=75)
+    x, tr = st.run(lookahead=False, single_layer=True)
+    check_stack(st, host(x), tr, lookahead=False)
+
+
+def test_serial_layer_threshold_mode():
+    s = synth.LayerShape(d=1032, N=1500, h=6, dh=128, n=300, r=136, dtype="f16")
+    st = Stack(s, 1, 22, k_A=0, k_M=0, mode=dj.DJV_THRESHOLD, t_A=0.6, t_M=0.7)
+    x, tr = st.run(lookahead=False, single_layer=True)
+    assert 0 < tr["counts"][0, 1] < s.N
+    check_stack(st, host(x), tr, lookahead=False)
+
+
+@pytest.mark.parametrize("lookahead", [True, False])
+def test_stack_small(lookahead):
+    s = synth.LayerShape(d=1032, N=1500, h=6, dh=128, n=300, r=136, dtype="f16")
+    st = Stack(s, 4, 23, k_A=2, k_M=75)
+    x, tr = st.run(lookahead=lookahead)
+    check_stack(st, host(x), tr, lookahead=lookahead)
+    # deterministic: the same step again gives the same bits
+    x2, tr2 = st.run(lookahead=lookahead)
+    assert np.array_equal(host(x), host(x2))
+
+
+def test_dense_stack_matches_oracle():
+    s = synth.LayerShape(d=1032, N=1500, h=6, dh=128, n=300, r=136, dtype="f16")
+    st = Stack(s, 2, 24, k_A=2, k_M=75)
+    t, tr = st.trace()
+    x = st.x0.clone()
+    dj.dejavu_stack_decode(st.m, st.desc, x, False, True, tr, st.ws)
+    torch.cuda.synchronize()
+    xs = host(t["x_in"])
+    for l in range(2):
+        Lw = O.LayerWeights(Wqkv=host(st.w[l]["Wqkv"]), Wo=host(st.w[l]["Wo"]), W1=host(st.w[l]["W1"]),
+                            b1=host(st.w[l]["b1"]), W2=host(st.w[l]["W2"]), K=st.K0[l], V=st.V0[l])
+        ref, _ = O.dense_layer(xs[l], Lw, s.n, st.scale)
+        nxt = host(x) if l == 1 else xs[l + 1]
+        assert rel_l2(nxt - xs[l], ref - xs[l]) < TOL["f16"]
+
+
+# ------------------------------------------------------------------------ full-size workloads
+def _workload_stack(name, L=None, B=None):
+    wl = configs.WORKLOADS[name]
+    s = wl.shape if B is None else wl.shape.with_(B=B)
+    return wl, Stack(s, L or wl.layers, 0, k_A=wl.k_A, k_M=wl.k_M)
+
+
+def test_opt125m_layer_fp32():
+    wl, st = _workload_stack("opt125m-1layer-fp32")
+    assert (st.k_A, st.k_M) == (3, 154)
+    x, tr = st.run(lookahead=False, single_layer=True)
+    check_stack(st, host(x), tr, lookahead=False)
+
+
+@pytest.mark.slow
+def test_opt175b_layer():
+    print("opt175b one layer", flush=True)
+    wl, st = _workload_stack("opt175b-1layer-fp16")
+    assert (st.k_A, st.k_M) == (20, 2458)
+    x, tr = st.run(lookahead=False, single_layer=True)
+    check_stack(st, host(x), tr, lookahead=False)
+
+
+@pytest.mark.slow
+def test_opt6_7b_lookahead_stack():
+    print("opt6.7b 3-layer lookahead", flush=True)
+    wl, st = _workload_stack("opt6.7b-32layers-fp16", L=3)
+    assert (st.k_A, st.k_M) == (7, 820)
+    x, tr = st.run(lookahead=True)
+    check_stack(st, host(x), tr, lookahead=True)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("B", [1, 4])
+def test_opt66b_layer(B):
+    print(f"opt66b one layer B={B}", flush=True)
+    wl, st = _workload_stack("opt66b-1layer-fp16", B=B)
+    x, tr = st.run(lookahead=False, single_layer=True)
+    check_stack(st, host(x), tr, lookahead=False)
+    if B == 4:
+        # union of per-token sets
+        assert tr["counts"][0, 1] >= st.k_M and tr["counts"][0, 0] >= st.k_A

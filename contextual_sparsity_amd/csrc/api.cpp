@@ -146,7 +146,7 @@ PredWs plan_predict(Arena& A, int B, int r, int n_out, bool need_z) {
 struct MlpWs { float* a; float* partial; int rpc; };
 MlpWs plan_mlp(Arena& A, int B, int d, int cap, bool f16) {
     MlpWs w;
-    w.a = A.take<float>((size_t)B * cap);
+    w.a = A.take<float>((size_t)B * (cap > 0 ? cap : 1));
     const int nch = axpy_chunks(cap, d, f16, &w.rpc);
     w.partial = A.take<float>((size_t)nch * B * d);
     return w;
@@ -155,108 +155,160 @@ MlpWs plan_mlp(Arena& A, int B, int d, int cap, bool f16) {
 struct MhaWs { float* q; float* part; float* H; float* partial; int rpc, chunk, nchunk_max; };
 MhaWs plan_mha(Arena& A, int B, int d, int dh, int cap, int n_cap, bool f16) {
     MhaWs w;
+    const int c = cap > 0 ? cap : 1;
     w.chunk = attn_chunk_for(f16, dh);
     w.nchunk_max = (n_cap + w.chunk - 1) / w.chunk;
-    w.q = A.take<float>((size_t)B * cap * dh);
-    w.part = A.take<float>((size_t)B * cap * w.nchunk_max * (dh + 2));
-    w.H = A.take<float>((size_t)B * cap * dh);
+    w.q = A.take<float>((size_t)B * c * dh);
+    w.part = A.take<float>((size_t)B * c * w.nchunk_max * (dh + 2));
+    w.H = A.take<float>((size_t)B * c * dh);
     const int nch = axpy_chunks(cap * dh, d, f16, &w.rpc);
     w.partial = A.take<float>((size_t)nch * B * d);
     return w;
 }
 
-int cap_of(int mode, int k, int n) { return mode == DJV_TOPK ? k : n; }
+// Capacity of a selected list: top-k keeps k per token, so a batch's union holds at most
+// min(n, B*k) units; a threshold can keep all n.
+int cap_of(int mode, int k, int n, int B) {
+    if (mode != DJV_TOPK) return n;
+    const long long c = (long long)k * B;
+    return c < n ? (int)c : n;
+}
 
+// Activation state and scratch of a layer or a stack of layers.
 struct LayerWs {
-    float* y[2];          // block inputs (ring of two for the lookahead schedule)
-    float* xa;            // x' = x + attention
-    float* y2;            // LN(x')
+    float* xs[2];                     // residual-stream ring: inputs of layers 1..L-1
+    float2* sx[2];                    // LayerNorm tile statistics of xs[i]
+    float2* s_in;                     // statistics of the caller's x (layer 0 input)
+    float* xm;                        // x' = x + attention
+    float2* sm;                       // statistics of x'
     int32_t* idxA[2]; int32_t* cntA[2];
     int32_t* idxM[2]; int32_t* cntM[2];
     MhaWs mha; MlpWs mlp;             // main-stream scratch
     PredWs predA, predM;              // predictor-stream scratch
+    int tiles;                        // LayerNorm statistic slices per row
 };
-LayerWs plan_layer(Arena& A, const djv_model& m) {
+LayerWs plan_layer(Arena& A, const djv_model& m, bool dense) {
     const bool f16 = m.wt == DJV_F16;
     LayerWs w;
-    for (int i = 0; i < 2; ++i) w.y[i] = A.take<float>((size_t)m.B * m.d);
-    w.xa = A.take<float>((size_t)m.B * m.d);
-    w.y2 = A.take<float>((size_t)m.B * m.d);
+    w.tiles = (m.d + kLnTile - 1) / kLnTile;
+    for (int i = 0; i < 2; ++i) {
+        w.xs[i] = A.take<float>((size_t)m.B * m.d);
+        w.sx[i] = A.take<float2>((size_t)m.B * w.tiles);
+    }
+    w.s_in = A.take<float2>((size_t)m.B * w.tiles);
+    w.xm = A.take<float>((size_t)m.B * m.d);
+    w.sm = A.take<float2>((size_t)m.B * w.tiles);
+    const int capA = dense ? m.h : cap_of(m.mode, m.k_A, m.h, m.B);
+    const int capM = dense ? m.N : cap_of(m.mode, m.k_M, m.N, m.B);
     for (int i = 0; i < 2; ++i) {
         w.idxA[i] = A.take<int32_t>(m.h);
         w.cntA[i] = A.take<int32_t>(1);
         w.idxM[i] = A.take<int32_t>(m.N);
         w.cntM[i] = A.take<int32_t>(1);
     }
-    w.mha = plan_mha(A, m.B, m.d, m.dh, cap_of(m.mode, m.k_A, m.h), m.n_cap, f16);
-    w.mlp = plan_mlp(A, m.B, m.d, cap_of(m.mode, m.k_M, m.N), f16);
-    w.predA = plan_predict(A, m.B, m.r, m.h, true);
-    w.predM = plan_predict(A, m.B, m.r, m.N, true);
+    w.mha = plan_mha(A, m.B, m.d, m.dh, capA, m.n_cap, f16);
+    w.mlp = plan_mlp(A, m.B, m.d, capM, f16);
+    if (!dense) {
+        w.predA = plan_predict(A, m.B, m.r, m.h, true);
+        w.predM = plan_predict(A, m.B, m.r, m.N, true);
+    } else {
+        w.predA = w.predM = PredWs{nullptr, nullptr, nullptr};
+    }
     return w;
 }
 
-// Dense-path scratch: all heads and all neurons.
-struct DenseWs { float* y; float* xa; float* y2; MhaWs mha; MlpWs mlp; };
-DenseWs plan_dense(Arena& A, const djv_model& m) {
-    const bool f16 = m.wt == DJV_F16;
-    DenseWs w;
-    w.y = A.take<float>((size_t)m.B * m.d);
-    w.xa = A.take<float>((size_t)m.B * m.d);
-    w.y2 = A.take<float>((size_t)m.B * m.d);
-    w.mha = plan_mha(A, m.B, m.d, m.dh, m.h, m.n_cap, f16);
-    w.mlp = plan_mlp(A, m.B, m.d, m.N, f16);
-    return w;
+RowInput plain_input(const float* y) {
+    RowInput in{};
+    in.y = y;
+    return in;
+}
+RowInput ln_input(const float* x, const float2* stats, const LayerWs& w, float eps) {
+    RowInput in{};
+    in.x = x;
+    in.stats = stats;
+    in.ntiles = w.tiles;
+    in.eps = eps;
+    return in;
 }
 
 // ------------------------------------------------------------------------------------
 // Kernel sequences shared by the entry points (arguments already validated)
 // ------------------------------------------------------------------------------------
-djv_status run_predict(bool f16, int B, int d, int r, int n_out, const float* y, const void* P1,
-                       const void* P2, int mode, int k, float t, int32_t* idx, int32_t* count,
-                       float* z, const PredWs& w, hipStream_t s) {
+struct PredJob {
+    const void* P1; const void* P2; int n_out;
+    int mode, k; float t;
+    int32_t* idx; int32_t* count; float* z;
+    const PredWs* w;
+};
+
+// One or two predictors reading the same input, in three launches: both first layers
+// (one GEMV launch), both second layers (one launch), both selections (one launch).
+djv_status run_predict(bool f16, int B, int d, int r, const RowInput& in, const PredJob* jobs,
+                       int njobs, hipStream_t s) {
     unsigned* flags = device_flags();
+    // both first layers in one launch, then both second layers, then both selections
     GemvArgs g{};
-    g.W = P1; g.cols = d; g.list = UnitList{nullptr, nullptr, r, r}; g.rpu = 1;
-    g.y = y; g.B = B; g.epi = kEpiRelu; g.out = w.u; g.ld = r; g.flags = flags;
-    g.prof = DJV_PROF_PRED_1;
+    g.nseg = njobs; g.cols = d; g.B = B; g.epi = kEpiRelu; g.flags = flags; g.prof = DJV_PROF_PRED_1;
+    for (int i = 0; i < njobs; ++i) {
+        GemvSeg& S = g.seg[i];
+        S.W = jobs[i].P1; S.list = UnitList{nullptr, nullptr, r, r}; S.rpu = 1; S.in = in;
+        S.out = jobs[i].w->u; S.ld = r;
+    }
     DJV_HIP(launch_gemv(f16, g, s));
     g = GemvArgs{};
-    g.W = P2; g.cols = r; g.list = UnitList{nullptr, nullptr, n_out, n_out}; g.rpu = 1;
-    g.y = w.u; g.B = B; g.epi = kEpiStore; g.out = z; g.ld = n_out; g.flags = flags;
-    g.prof = DJV_PROF_PRED_2;
+    g.nseg = njobs; g.cols = r; g.B = B; g.epi = kEpiStore; g.flags = flags; g.prof = DJV_PROF_PRED_2;
+    for (int i = 0; i < njobs; ++i) {
+        GemvSeg& S = g.seg[i];
+        S.W = jobs[i].P2; S.list = UnitList{nullptr, nullptr, jobs[i].n_out, jobs[i].n_out};
+        S.rpu = 1; S.in = plain_input(jobs[i].w->u); S.out = jobs[i].z; S.ld = jobs[i].n_out;
+    }
     DJV_HIP(launch_gemv(f16, g, s));
-    SelectJob j{z, n_out, mode, k, mode == DJV_THRESHOLD ? tau_key(t) : 0u, w.bits, idx, count};
-    DJV_HIP(launch_select(&j, 1, B, s, DJV_PROF_SELECT));
+    SelectJob sj[2];
+    for (int i = 0; i < njobs; ++i) {
+        const PredJob& J = jobs[i];
+        sj[i] = SelectJob{J.z, J.n_out, J.mode, J.k, J.mode == DJV_THRESHOLD ? tau_key(J.t) : 0u,
+                          J.w->bits, J.idx, J.count};
+    }
+    DJV_HIP(launch_select(sj, njobs, B, s, DJV_PROF_SELECT));
     return DJV_OK;
 }
 
-djv_status run_mlp(bool f16, int B, int d, int N, const float* y, const void* W1, const void* b1,
-                   const void* W2, const int32_t* idx, const int32_t* count, int cap,
-                   const float* resid, float* out, const MlpWs& w, hipStream_t s) {
+// out = resid + MLP_S(in): gather-GEMV over the kept W1 rows, then row-axpy over the kept
+// W2 rows.  stats (optional) receives the tile statistics of out.
+djv_status run_mlp(bool f16, int B, int d, int N, const RowInput& in, const void* W1,
+                   const void* b1, const void* W2, const int32_t* idx, const int32_t* count,
+                   int cap, const float* resid, float* out, float2* stats, const MlpWs& w,
+                   hipStream_t s) {
     unsigned* flags = device_flags();
     const UnitList list{idx, count, cap, N};
     GemvArgs g{};
-    g.W = W1; g.cols = d; g.list = list; g.rpu = 1; g.y = y; g.B = B; g.epi = kEpiBiasRelu;
-    g.out = w.a; g.ld = cap; g.bias = b1; g.flags = flags; g.prof = DJV_PROF_MLP_UP;
+    g.nseg = 1; g.cols = d; g.B = B; g.epi = kEpiBiasRelu; g.bias = b1; g.flags = flags;
+    g.prof = DJV_PROF_MLP_UP;
+    g.seg[0].W = W1; g.seg[0].list = list; g.seg[0].rpu = 1; g.seg[0].in = in;
+    g.seg[0].out = w.a; g.seg[0].ld = cap;
     DJV_HIP(launch_gemv(f16, g, s));
     AxpyArgs x{};
     x.W = W2; x.cols = d; x.list = list; x.rpu = 1; x.coef = w.a; x.ldc = cap; x.B = B;
-    x.partial = w.partial; x.rows_per_chunk = w.rpc; x.resid = resid; x.out = out; x.flags = flags;
-    x.prof = DJV_PROF_MLP_DOWN;
+    x.partial = w.partial; x.rows_per_chunk = w.rpc; x.resid = resid;
+    x.out = out; x.stats = stats; x.flags = flags; x.prof = DJV_PROF_MLP_DOWN;
     DJV_HIP(launch_axpy(f16, x, s));
     return DJV_OK;
 }
 
-djv_status run_mha(bool f16, int B, int d, int h, int dh, int n, int n_cap, const float* y,
+// out = resid + MHA_S(in), appending the kept heads' K/V at position n: head-sparse QKV
+// GEMV, split-position attention and its merge, row-axpy over the kept
+// heads' W_O rows.  stats (optional) receives the tile statistics of out.
+djv_status run_mha(bool f16, int B, int d, int h, int dh, int n, int n_cap, const RowInput& in,
                    const void* Wqkv, const void* Wo, void* Kc, void* Vc, const int32_t* idx,
                    const int32_t* count, int cap, float scale, const float* resid, float* out,
-                   const MhaWs& w, hipStream_t s) {
+                   float2* stats, const MhaWs& w, hipStream_t s) {
     unsigned* flags = device_flags();
     const UnitList list{idx, count, cap, h};
     GemvArgs g{};
-    g.W = Wqkv; g.cols = d; g.list = list; g.rpu = 3 * dh; g.y = y; g.B = B; g.epi = kEpiQkv;
-    g.out = w.q; g.ld = cap * dh; g.Kc = Kc; g.Vc = Vc; g.h = h; g.dh = dh; g.n = n;
-    g.n_cap = n_cap; g.flags = flags; g.prof = DJV_PROF_QKV;
+    g.nseg = 1; g.cols = d; g.B = B; g.epi = kEpiQkv; g.Kc = Kc; g.Vc = Vc; g.h = h; g.dh = dh;
+    g.n = n; g.n_cap = n_cap; g.flags = flags; g.prof = DJV_PROF_QKV;
+    g.seg[0].W = Wqkv; g.seg[0].list = list; g.seg[0].rpu = 3 * dh; g.seg[0].in = in;
+    g.seg[0].out = w.q; g.seg[0].ld = cap * dh;
     DJV_HIP(launch_gemv(f16, g, s));
     AttnArgs at{};
     at.Kc = Kc; at.Vc = Vc; at.list = list; at.h = h; at.dh = dh; at.n = n; at.n_cap = n_cap;
@@ -266,8 +318,7 @@ djv_status run_mha(bool f16, int B, int d, int h, int dh, int n, int n_cap, cons
     DJV_HIP(launch_attention(f16, at, s));
     AxpyArgs x{};
     x.W = Wo; x.cols = d; x.list = list; x.rpu = dh; x.coef = w.H; x.ldc = cap * dh; x.B = B;
-    x.partial = w.partial; x.rows_per_chunk = w.rpc; x.resid = resid; x.out = out; x.flags = flags;
-    x.prof = DJV_PROF_O_PROJ;
+    x.partial = w.partial; x.rows_per_chunk = w.rpc; x.resid = resid; x.out = out; x.stats = stats; x.flags = flags; x.prof = DJV_PROF_O_PROJ;
     DJV_HIP(launch_axpy(f16, x, s));
     return DJV_OK;
 }
@@ -281,6 +332,8 @@ djv_status check_model(const djv_model* m) {
     DJV_REQUIRE(m->N >= 1 && m->h >= 1, DJV_EINVAL, "N and h must be >= 1");
     DJV_REQUIRE(m->dh == 64 || m->dh == 128, DJV_EUNSUPPORTED, "dh must be 64 or 128 (got %d)", m->dh);
     DJV_REQUIRE(m->n >= 0 && m->n < m->n_cap, DJV_EINVAL, "need 0 <= n < n_cap (n = %d, n_cap = %d)", m->n, m->n_cap);
+    DJV_REQUIRE((m->n_cap + attn_chunk_for(m->wt == DJV_F16, m->dh) - 1) / attn_chunk_for(m->wt == DJV_F16, m->dh)
+                    <= kAttnMaxChunks, DJV_EUNSUPPORTED, "n_cap = %d is too long", m->n_cap);
     DJV_REQUIRE(std::isfinite(m->scale), DJV_EINVAL, "scale must be finite");
     DJV_REQUIRE(m->eps > 0.f && std::isfinite(m->eps), DJV_EINVAL, "eps must be > 0");
     DJV_TRY(check_select(m->h, m->mode, m->k_A, m->t_A, "head selection"));
@@ -308,11 +361,10 @@ djv_status check_layer(const djv_layer* L, bool dense) {
 
 size_t layer_ws_bytes(const djv_model& m) {
     Arena A(nullptr);
-    plan_layer(A, m);
-    size_t s = A.off;
+    plan_layer(A, m, false);
     Arena D(nullptr);
-    plan_dense(D, m);
-    return s > D.off ? s : D.off;
+    plan_layer(D, m, true);
+    return A.off > D.off ? A.off : D.off;
 }
 
 djv_status copy_async(void* dst, const void* src, size_t bytes, hipStream_t s) {
@@ -325,7 +377,7 @@ djv_status copy_async(void* dst, const void* src, size_t bytes, hipStream_t s) {
 djv_status trace_sets(const djv_trace* tr, const djv_model& m, int l, const LayerWs& w, int buf,
                       hipStream_t s) {
     if (!tr) return DJV_OK;
-    const int capA = cap_of(m.mode, m.k_A, m.h), capM = cap_of(m.mode, m.k_M, m.N);
+    const int capA = cap_of(m.mode, m.k_A, m.h, m.B), capM = cap_of(m.mode, m.k_M, m.N, m.B);
     if (tr->sets_A) DJV_TRY(copy_async(tr->sets_A + (size_t)l * m.h, w.idxA[buf], capA * 4, s));
     if (tr->sets_M) DJV_TRY(copy_async(tr->sets_M + (size_t)l * m.N, w.idxM[buf], capM * 4, s));
     if (tr->counts) {
@@ -348,35 +400,66 @@ float* zM_of(const djv_trace* tr, const djv_model& m, int l, const LayerWs& w) {
     return (tr && tr->z_M) ? tr->z_M + (size_t)l * m.B * m.N : w.predM.z;
 }
 
-// Predicts the head set of layer l from y into buffer `buf`.
-djv_status predict_A(const djv_model& m, const djv_layer& L, const float* y, const LayerWs& w,
-                     int buf, const djv_trace* tr, int l, hipStream_t s) {
-    return run_predict(m.wt == DJV_F16, m.B, m.d, m.r, m.h, y, L.P1_A, L.P2_A, m.mode, m.k_A,
-                       m.t_A, w.idxA[buf], w.cntA[buf], zA_of(tr, m, l, w), w.predA, s);
+PredJob job_A(const djv_model& m, const djv_layer& L, const LayerWs& w, int buf,
+              const djv_trace* tr, int l) {
+    return PredJob{L.P1_A, L.P2_A, m.h, m.mode, m.k_A, m.t_A, w.idxA[buf], w.cntA[buf],
+                   zA_of(tr, m, l, w), &w.predA};
 }
-// Predicts the neuron set of layer l from y into buffer `buf`.
-djv_status predict_M(const djv_model& m, const djv_layer& L, const float* y, const LayerWs& w,
-                     int buf, const djv_trace* tr, int l, hipStream_t s) {
-    return run_predict(m.wt == DJV_F16, m.B, m.d, m.r, m.N, y, L.P1_M, L.P2_M, m.mode, m.k_M,
-                       m.t_M, w.idxM[buf], w.cntM[buf], zM_of(tr, m, l, w), w.predM, s);
+PredJob job_M(const djv_model& m, const djv_layer& L, const LayerWs& w, int buf,
+              const djv_trace* tr, int l) {
+    return PredJob{L.P1_M, L.P2_M, m.N, m.mode, m.k_M, m.t_M, w.idxM[buf], w.cntM[buf],
+                   zM_of(tr, m, l, w), &w.predM};
 }
 
-// Attention then MLP of layer l with the sets in buffer `buf`; y = LN(x) given.  With
-// predict_M_here the neuron set is predicted from LN(x') in between (serial schedule).
-djv_status layer_body(const djv_model& m, const djv_layer& L, float* x, const float* y,
-                      const LayerWs& w, int buf, bool predict_M_here, const djv_trace* tr, int l,
-                      hipStream_t s) {
+// Input and output of layer l in a stack of L: layer 0 reads the caller's x, the last
+// layer writes it, the others use the two-entry ring.
+struct LayerIO {
+    const float* x_in; const float2* s_in;
+    float* x_out; float2* s_out;
+};
+LayerIO layer_io(float* x, const LayerWs& w, int l, int L) {
+    LayerIO io;
+    io.x_in = l == 0 ? x : w.xs[l & 1];
+    io.s_in = l == 0 ? w.s_in : w.sx[l & 1];
+    io.x_out = l == L - 1 ? x : w.xs[(l + 1) & 1];
+    io.s_out = l == L - 1 ? nullptr : w.sx[(l + 1) & 1];
+    return io;
+}
+
+// Device count of a selected list, or nullptr when it is known on the host to equal the
+// capacity (top-k with one sequence keeps exactly k), which saves kernels a dependent read.
+const int32_t* count_of(const djv_model& m, const int32_t* count) {
+    return (m.mode == DJV_TOPK && m.B == 1) ? nullptr : count;
+}
+
+// Attention then MLP of layer l with the sets in buffer `buf`.  With serial set, the
+// neuron set is predicted from LN(x') in between (the order of the naive block).
+djv_status layer_body(const djv_model& m, const djv_layer& L, const LayerIO& io, const LayerWs& w,
+                      int buf, bool serial, const djv_trace* tr, int l, hipStream_t s) {
     const bool f16 = m.wt == DJV_F16;
-    DJV_TRY(run_mha(f16, m.B, m.d, m.h, m.dh, m.n, m.n_cap, y, L.Wqkv, L.Wo, L.Kc, L.Vc,
-                    w.idxA[buf], w.cntA[buf], cap_of(m.mode, m.k_A, m.h), m.scale, x, w.xa,
-                    w.mha, s));
+    DJV_TRY(run_mha(f16, m.B, m.d, m.h, m.dh, m.n, m.n_cap, ln_input(io.x_in, io.s_in, w, m.eps),
+                    L.Wqkv, L.Wo, L.Kc, L.Vc, w.idxA[buf], count_of(m, w.cntA[buf]),
+                    cap_of(m.mode, m.k_A, m.h, m.B), m.scale, io.x_in, w.xm, w.sm, w.mha, s));
     if (tr && tr->x_mid)
-        DJV_TRY(copy_async(tr->x_mid + (size_t)l * m.B * m.d, w.xa, (size_t)m.B * m.d * 4, s));
-    DJV_HIP(launch_layernorm(m.B, m.d, w.xa, w.y2, m.eps, s));
-    if (predict_M_here) DJV_TRY(predict_M(m, L, w.y2, w, buf, tr, l, s));
-    DJV_TRY(run_mlp(f16, m.B, m.d, m.N, w.y2, L.W1, L.b1, L.W2, w.idxM[buf], w.cntM[buf],
-                    cap_of(m.mode, m.k_M, m.N), w.xa, x, w.mlp, s));
+        DJV_TRY(copy_async(tr->x_mid + (size_t)l * m.B * m.d, w.xm, (size_t)m.B * m.d * 4, s));
+    const RowInput in_m = ln_input(w.xm, w.sm, w, m.eps);
+    if (serial) {
+        const PredJob jm = job_M(m, L, w, buf, tr, l);
+        DJV_TRY(run_predict(f16, m.B, m.d, m.r, in_m, &jm, 1, s));
+    }
+    DJV_TRY(run_mlp(f16, m.B, m.d, m.N, in_m, L.W1, L.b1, L.W2, w.idxM[buf], count_of(m, w.cntM[buf]),
+                    cap_of(m.mode, m.k_M, m.N, m.B), w.xm, io.x_out, io.s_out, w.mlp, s));
     return DJV_OK;
+}
+
+// One serial layer (head set from LN(x), neuron set from LN(x')).
+djv_status serial_layer(const djv_model& m, const djv_layer& L, const LayerIO& io,
+                        const LayerWs& w, const djv_trace* tr, int l, hipStream_t s) {
+    DJV_TRY(trace_x(tr, m, l, io.x_in, s));
+    const PredJob ja = job_A(m, L, w, 0, tr, l);
+    DJV_TRY(run_predict(m.wt == DJV_F16, m.B, m.d, m.r, ln_input(io.x_in, io.s_in, w, m.eps), &ja, 1, s));
+    DJV_TRY(layer_body(m, L, io, w, 0, true, tr, l, s));
+    return trace_sets(tr, m, l, w, 0, s);
 }
 
 }  // namespace
@@ -388,7 +471,7 @@ extern "C" {
 
 const char* dejavu_last_error(void) { return g_err.c_str(); }
 
-const char* dejavu_version(void) { return "dejavu-mi355x 0.1 (gfx950)"; }
+const char* dejavu_version(void) { return "dejavu-mi355x 0.2 (gfx950)"; }
 
 djv_status dejavu_workspace_bytes(int B, int d, int N, int h, int dh, int r, int n_cap,
                                   size_t* bytes) {
@@ -436,6 +519,7 @@ djv_status dejavu_workspace_bytes_model(const djv_model* m, size_t* bytes) {
 
 djv_status dejavu_layernorm(int B, int d, const float* x, float* y, float eps, void* stream) {
     DJV_REQUIRE(B >= 1 && d >= 1, DJV_EINVAL, "B and d must be >= 1");
+    DJV_REQUIRE(d <= 16384, DJV_EUNSUPPORTED, "d = %d exceeds 16384", d);
     DJV_REQUIRE(eps > 0.f && std::isfinite(eps), DJV_EINVAL, "eps must be > 0");
     DJV_TRY(check_ptr(x, "x"));
     DJV_TRY(check_ptr(y, "y"));
@@ -479,10 +563,9 @@ djv_status dejavu_predict(djv_dtype wt, int B, int d, int r, int n_out, const fl
     plan_predict(sz, B, r, n_out, logits == nullptr);
     DJV_TRY(check_ws(ws, ws_bytes, sz.off));
     Arena A(ws);
-    PredWs w = plan_predict(A, B, r, n_out, logits == nullptr);
-    float* z = logits ? logits : w.z;
-    return run_predict(wt == DJV_F16, B, d, r, n_out, y, P1, P2, mode, k, t, idx, count, z, w,
-                       (hipStream_t)stream);
+    const PredWs w = plan_predict(A, B, r, n_out, logits == nullptr);
+    const PredJob j{P1, P2, n_out, (int)mode, k, t, idx, count, logits ? logits : w.z, &w};
+    return run_predict(wt == DJV_F16, B, d, r, plain_input(y), &j, 1, (hipStream_t)stream);
 }
 
 static djv_status mlp_common(djv_dtype wt, int B, int d, int N, const float* y, const void* W1,
@@ -505,8 +588,9 @@ static djv_status mlp_common(djv_dtype wt, int B, int d, int N, const float* y, 
     plan_mlp(sz, B, d, cap, f16);
     DJV_TRY(check_ws(ws, ws_bytes, sz.off));
     Arena A(ws);
-    MlpWs w = plan_mlp(A, B, d, cap, f16);
-    return run_mlp(f16, B, d, N, y, W1, b1, W2, idx, count, cap, resid, out, w, (hipStream_t)stream);
+    const MlpWs w = plan_mlp(A, B, d, cap, f16);
+    return run_mlp(f16, B, d, N, plain_input(y), W1, b1, W2, idx, count, cap, resid, out, nullptr,
+                   w, (hipStream_t)stream);
 }
 
 djv_status dejavu_sparse_mlp(djv_dtype wt, int B, int d, int N, const float* y, const void* W1,
@@ -536,6 +620,8 @@ static djv_status mha_common(djv_dtype wt, int B, int d, int h, int dh, int n, i
     DJV_REQUIRE(h >= 1, DJV_EINVAL, "h must be >= 1");
     DJV_REQUIRE(dh == 64 || dh == 128, DJV_EUNSUPPORTED, "dh must be 64 or 128 (got %d)", dh);
     DJV_REQUIRE(n >= 0 && n < n_cap, DJV_EINVAL, "need 0 <= n < n_cap (n = %d, n_cap = %d)", n, n_cap);
+    DJV_REQUIRE((n_cap + attn_chunk_for(wt == DJV_F16, dh) - 1) / attn_chunk_for(wt == DJV_F16, dh)
+                    <= kAttnMaxChunks, DJV_EUNSUPPORTED, "n_cap = %d is too long", n_cap);
     DJV_REQUIRE(cap >= 1 && cap <= h, DJV_EINVAL, "cap = %d outside [1, h = %d]", cap, h);
     DJV_REQUIRE(std::isfinite(scale), DJV_EINVAL, "scale must be finite");
     DJV_TRY(check_ptr(y, "y"));
@@ -550,9 +636,9 @@ static djv_status mha_common(djv_dtype wt, int B, int d, int h, int dh, int n, i
     plan_mha(sz, B, d, dh, cap, n_cap, f16);
     DJV_TRY(check_ws(ws, ws_bytes, sz.off));
     Arena A(ws);
-    MhaWs w = plan_mha(A, B, d, dh, cap, n_cap, f16);
-    return run_mha(f16, B, d, h, dh, n, n_cap, y, Wqkv, Wo, Kc, Vc, idx, count, cap, scale, resid,
-                   out, w, (hipStream_t)stream);
+    const MhaWs w = plan_mha(A, B, d, dh, cap, n_cap, f16);
+    return run_mha(f16, B, d, h, dh, n, n_cap, plain_input(y), Wqkv, Wo, Kc, Vc, idx, count, cap,
+                   scale, resid, out, nullptr, w, (hipStream_t)stream);
 }
 
 djv_status dejavu_sparse_mha(djv_dtype wt, int B, int d, int h, int dh, int n, int n_cap,
@@ -582,12 +668,9 @@ djv_status dejavu_sparse_layer(const djv_model* m, const djv_layer* layer, float
     DJV_TRY(check_ws(ws, ws_bytes, layer_ws_bytes(*m)));
     hipStream_t s = (hipStream_t)stream;
     Arena A(ws);
-    const LayerWs w = plan_layer(A, *m);
-    DJV_TRY(trace_x(trace, *m, 0, x, s));
-    DJV_HIP(launch_layernorm(m->B, m->d, x, w.y[0], m->eps, s));
-    DJV_TRY(predict_A(*m, *layer, w.y[0], w, 0, trace, 0, s));
-    DJV_TRY(layer_body(*m, *layer, x, w.y[0], w, 0, true, trace, 0, s));
-    return trace_sets(trace, *m, 0, w, 0, s);
+    const LayerWs w = plan_layer(A, *m, false);
+    DJV_HIP(launch_ln_stats(m->B, m->d, x, w.s_in, s));
+    return serial_layer(*m, *layer, layer_io(x, w, 0, 1), w, trace, 0, s);
 }
 
 djv_status dejavu_stack_decode(const djv_model* m, const djv_layer* layers, int L, float* x,
@@ -601,37 +684,34 @@ djv_status dejavu_stack_decode(const djv_model* m, const djv_layer* layers, int 
     DJV_TRY(check_ws(ws, ws_bytes, layer_ws_bytes(*m)));
     hipStream_t sm = (hipStream_t)s_main, sp = (hipStream_t)s_pred;
     const bool f16 = m->wt == DJV_F16;
+    Arena A(ws);
+    const LayerWs w = plan_layer(A, *m, dense != 0);
+    DJV_HIP(launch_ln_stats(m->B, m->d, x, w.s_in, sm));
 
     if (dense) {
-        Arena A(ws);
-        const DenseWs w = plan_dense(A, *m);
         for (int l = 0; l < L; ++l) {
             const djv_layer& Ly = layers[l];
-            DJV_TRY(trace_x(trace, *m, l, x, sm));
-            DJV_HIP(launch_layernorm(m->B, m->d, x, w.y, m->eps, sm));
-            DJV_TRY(run_mha(f16, m->B, m->d, m->h, m->dh, m->n, m->n_cap, w.y, Ly.Wqkv, Ly.Wo,
-                            Ly.Kc, Ly.Vc, nullptr, nullptr, m->h, m->scale, x, w.xa, w.mha, sm));
-            DJV_HIP(launch_layernorm(m->B, m->d, w.xa, w.y2, m->eps, sm));
-            DJV_TRY(run_mlp(f16, m->B, m->d, m->N, w.y2, Ly.W1, Ly.b1, Ly.W2, nullptr, nullptr,
-                            m->N, w.xa, x, w.mlp, sm));
+            const LayerIO io = layer_io(x, w, l, L);
+            DJV_TRY(trace_x(trace, *m, l, io.x_in, sm));
+            DJV_TRY(run_mha(f16, m->B, m->d, m->h, m->dh, m->n, m->n_cap,
+                            ln_input(io.x_in, io.s_in, w, m->eps), Ly.Wqkv, Ly.Wo, Ly.Kc, Ly.Vc,
+                            nullptr, nullptr, m->h, m->scale, io.x_in, w.xm, w.sm, w.mha, sm));
+            if (trace && trace->x_mid)
+                DJV_TRY(copy_async(trace->x_mid + (size_t)l * m->B * m->d, w.xm,
+                                   (size_t)m->B * m->d * 4, sm));
+            DJV_TRY(run_mlp(f16, m->B, m->d, m->N, ln_input(w.xm, w.sm, w, m->eps), Ly.W1, Ly.b1,
+                            Ly.W2, nullptr, nullptr, m->N, w.xm, io.x_out, io.s_out, w.mlp, sm));
         }
         return DJV_OK;
     }
 
-    Arena A(ws);
-    const LayerWs w = plan_layer(A, *m);
     if (!lookahead) {
-        for (int l = 0; l < L; ++l) {
-            DJV_TRY(trace_x(trace, *m, l, x, sm));
-            DJV_HIP(launch_layernorm(m->B, m->d, x, w.y[0], m->eps, sm));
-            DJV_TRY(predict_A(*m, layers[l], w.y[0], w, 0, trace, l, sm));
-            DJV_TRY(layer_body(*m, layers[l], x, w.y[0], w, 0, true, trace, l, sm));
-            DJV_TRY(trace_sets(trace, *m, l, w, 0, sm));
-        }
+        for (int l = 0; l < L; ++l)
+            DJV_TRY(serial_layer(*m, layers[l], layer_io(x, w, l, L), w, trace, l, sm));
         return DJV_OK;
     }
 
-    // Lookahead schedule: S^{l+1} from y_l on the predictor stream while layer l runs.
+    // Lookahead schedule: S^{l+1} from LN(x_l) on the predictor stream while layer l runs.
     hipEvent_t evY = nullptr, evS = nullptr;
     DJV_HIP(hipEventCreateWithFlags(&evY, hipEventDisableTiming));
     if (hipEventCreateWithFlags(&evS, hipEventDisableTiming) != hipSuccess) {
@@ -643,27 +723,28 @@ djv_status dejavu_stack_decode(const djv_model* m, const djv_layer* layers, int 
         ~Guard() { (void)hipEventDestroy(a); (void)hipEventDestroy(b); }
     } guard{evY, evS};
 
-    DJV_TRY(trace_x(trace, *m, 0, x, sm));
-    DJV_HIP(launch_layernorm(m->B, m->d, x, w.y[0], m->eps, sm));
-    DJV_TRY(predict_A(*m, layers[0], w.y[0], w, 0, trace, 0, sm));
-    DJV_TRY(predict_M(*m, layers[0], w.y[0], w, 0, trace, 0, sm));
+    {
+        // layer 0's sets, serially from LN(x_0)
+        const LayerIO io0 = layer_io(x, w, 0, L);
+        const PredJob j2[2] = {job_A(*m, layers[0], w, 0, trace, 0), job_M(*m, layers[0], w, 0, trace, 0)};
+        DJV_TRY(run_predict(f16, m->B, m->d, m->r, ln_input(io0.x_in, io0.s_in, w, m->eps), j2, 2, sm));
+    }
     DJV_HIP(hipEventRecord(evY, sm));
     for (int l = 0; l < L; ++l) {
         const int cur = l & 1, nxt = (l + 1) & 1;
+        const LayerIO io = layer_io(x, w, l, L);
         if (l >= 1) DJV_HIP(hipStreamWaitEvent(sm, evS, 0));  // S^l ready
+        DJV_TRY(trace_x(trace, *m, l, io.x_in, sm));
         DJV_TRY(trace_sets(trace, *m, l, w, cur, sm));
         if (l + 1 < L) {
-            DJV_HIP(hipStreamWaitEvent(sp, evY, 0));           // y_l ready, buffer nxt free
-            DJV_TRY(predict_A(*m, layers[l + 1], w.y[cur], w, nxt, trace, l + 1, sp));
-            DJV_TRY(predict_M(*m, layers[l + 1], w.y[cur], w, nxt, trace, l + 1, sp));
+            DJV_HIP(hipStreamWaitEvent(sp, evY, 0));           // x_l ready, buffer nxt free
+            const PredJob j2[2] = {job_A(*m, layers[l + 1], w, nxt, trace, l + 1),
+                                   job_M(*m, layers[l + 1], w, nxt, trace, l + 1)};
+            DJV_TRY(run_predict(f16, m->B, m->d, m->r, ln_input(io.x_in, io.s_in, w, m->eps), j2, 2, sp));
             DJV_HIP(hipEventRecord(evS, sp));
         }
-        DJV_TRY(layer_body(*m, layers[l], x, w.y[cur], w, cur, false, trace, l, sm));
-        if (l + 1 < L) {
-            DJV_TRY(trace_x(trace, *m, l + 1, x, sm));
-            DJV_HIP(launch_layernorm(m->B, m->d, x, w.y[nxt], m->eps, sm));
-            DJV_HIP(hipEventRecord(evY, sm));
-        }
+        DJV_TRY(layer_body(*m, layers[l], io, w, cur, false, trace, l, sm));
+        if (l + 1 < L) DJV_HIP(hipEventRecord(evY, sm));
     }
     return DJV_OK;
 }

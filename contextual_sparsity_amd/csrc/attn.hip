@@ -7,8 +7,10 @@
 // A kept head has only n+1 keys, and a few dozen heads cannot fill 256 compute units,
 // so the positions are cut into chunks: block (sequence b, head slot u, chunk c)
 // computes for its positions the running max m, the sum l of exp(s - m) and the
-// weighted value sum; a merge kernel rescales the chunks to the global max and divides.
-// Scores use max subtraction, which cancels exactly between numerator and D.
+// weighted value sum; a merge kernel (one block per head) rescales the chunks to the
+// global max, divides and writes H_i.  Scores use max subtraction, which cancels exactly
+// between numerator and D.  Keys and values of the chunk are all requested before the
+// first score is formed.
 //
 // Lanes: a key/value row is dh elements = LPP lanes x one 16-byte vector; a block of 256
 // threads covers 256/LPP positions per pass and makes 8 passes per chunk.
@@ -55,12 +57,17 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < E; ++e) qs[e] = q[e] * a.scale;
 
-    // scores of this chunk
-    Vec16 kv[kPasses];
+    // keys and values of this chunk, all in flight at once
+    Vec16 kv[kPasses], vv[kPasses];
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
         const int t = t0 + p * PPI + grp;
-        kv[p] = t < t1 ? ldg16(Kb + (size_t)t * DH * sizeof(T) + sl * 16) : Vec16{{0u, 0u, 0u, 0u}};
+        kv[p] = t < t1 ? ldg16_nt(Kb + (size_t)t * DH * sizeof(T) + sl * 16) : Vec16{{0u, 0u, 0u, 0u}};
+    }
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+        const int t = t0 + p * PPI + grp;
+        vv[p] = t < t1 ? ldg16_nt(Vb + (size_t)t * DH * sizeof(T) + sl * 16) : Vec16{{0u, 0u, 0u, 0u}};
     }
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
@@ -96,18 +103,13 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     l = wred[0] + wred[1] + wred[2] + wred[3];
 
     // weighted values
-#pragma unroll
-    for (int p = 0; p < kPasses; ++p) {
-        const int t = t0 + p * PPI + grp;
-        kv[p] = t < t1 ? ldg16(Vb + (size_t)t * DH * sizeof(T) + sl * 16) : Vec16{{0u, 0u, 0u, 0u}};
-    }
     float acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.f;
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
         float f[E];
-        unpack<T>(kv[p], f);
+        unpack<T>(vv[p], f);
         const float w = sc[p * PPI + grp];
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[e] = fmaf(w, f[e], acc[e]);
@@ -127,30 +129,57 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     }
 }
 
-// H[b, u] = sum_c e^{m_c - M} acc_c / sum_c e^{m_c - M} l_c over the chunks.
+// H[b, u] = sum_c e^{m_c - M} acc_c / sum_c e^{m_c - M} l_c over the chunks of a head.
+// One block of dh threads per (sequence, head slot); chunk maxima and weights go through
+// LDS, and each thread issues its column's loads in batches of 8 before adding.
 template <int DH>
 __global__ __launch_bounds__(DH) void attn_merge_kernel(AttnArgs a) {
+    __shared__ float cw[kAttnMaxChunks];
+    __shared__ float red[DH / kWave];
     const int cap = a.list.cap;
     const int b = blockIdx.x / cap, u = blockIdx.x - b * cap;
+    const int tid = threadIdx.x;
     const int count = read_count(a.list, nullptr);
     if (u >= count) return;
     float* H = a.H + ((size_t)b * cap + u) * DH;
-    const int unit = unit_of(a.list, u, nullptr);
-    if (unit < 0) {
-        H[threadIdx.x] = 0.f;
+    if (unit_of(a.list, u, nullptr) < 0) {
+        H[tid] = 0.f;
         return;
     }
-    const float* part = a.part + ((size_t)b * cap + u) * a.nchunk * (DH + 2);
-    float M = -INFINITY;
-    for (int c = 0; c < a.nchunk; ++c) M = fmaxf(M, part[c * (DH + 2)]);
-    float L = 0.f, s = 0.f;
-    for (int c = 0; c < a.nchunk; ++c) {
-        const float* p = part + c * (DH + 2);
-        const float f = __expf(p[0] - M);
-        L = fmaf(p[1], f, L);
-        s = fmaf(p[2 + threadIdx.x], f, s);
+    const float* hp = a.part + ((size_t)b * cap + u) * a.nchunk * (DH + 2);
+    float m = -INFINITY;
+    for (int c = tid; c < a.nchunk; c += DH) {
+        cw[c] = hp[(size_t)c * (DH + 2)];
+        m = fmaxf(m, cw[c]);
     }
-    H[threadIdx.x] = s / L;
+    m = wave_max(m);
+    if (tid % kWave == 0) red[tid / kWave] = m;
+    __syncthreads();
+    float M = red[0];
+#pragma unroll
+    for (int q = 1; q < DH / kWave; ++q) M = fmaxf(M, red[q]);
+    for (int c = tid; c < a.nchunk; c += DH) cw[c] = __expf(cw[c] - M);
+    __syncthreads();
+    float L = 0.f, acc = 0.f;
+    int c = 0;
+    for (; c + 8 <= a.nchunk; c += 8) {
+        float lv[8], av[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            lv[k] = hp[(size_t)(c + k) * (DH + 2) + 1];
+            av[k] = hp[(size_t)(c + k) * (DH + 2) + 2 + tid];
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            L = fmaf(lv[k], cw[c + k], L);
+            acc = fmaf(av[k], cw[c + k], acc);
+        }
+    }
+    for (; c < a.nchunk; ++c) {
+        L = fmaf(hp[(size_t)c * (DH + 2) + 1], cw[c], L);
+        acc = fmaf(hp[(size_t)c * (DH + 2) + 2 + tid], cw[c], acc);
+    }
+    H[tid] = acc / L;
 }
 
 template <typename T, int DH>

@@ -90,6 +90,31 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// Sum over a block of NT threads (NT a multiple of 64); red holds NT/64 floats.
+template <int NT>
+__device__ __forceinline__ float block_sum(float v, float* red) {
+    v = wave_sum(v);
+    if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = v;
+    __syncthreads();
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < NT / kWave; ++q) s += red[q];
+    __syncthreads();
+    return s;
+}
+
+// LayerNorm statistics travel as (mean, M2) of each kLnTile-column slice of a row.
+constexpr int kLnTile = 64;
+
+// Order-preserving key of an fp32 score: larger score, larger key; -0 = +0; NaN ranks as
+// -inf.
+__device__ __forceinline__ uint32_t score_key(float z) {
+    uint32_t u = __float_as_uint(z);
+    if (z != z) u = 0xFF800000u;
+    if ((u & 0x7FFFFFFFu) == 0u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 __device__ __forceinline__ void set_flag(unsigned* flags, unsigned bit) {
     if (flags) atomicOr(flags, bit);
 }
@@ -141,16 +166,33 @@ enum GemvEpi : int {
     kEpiQkv = 3,        // q -> out, k/v -> cache position n (rounded to the cache dtype)
 };
 
-struct GemvArgs {
-    const void* W;        // weights, rows of `cols` elements
-    int cols;             // row length in elements (d or r)
+// Activation rows fed to a GEMV: either ready rows y, or LayerNorm(x) applied on the fly
+// from per-tile statistics of x (see LnTiles).
+struct RowInput {
+    const float* y;       // [B, cols] ready input; when nullptr, LN(x) is used
+    const float* x;       // [B, cols] residual stream
+    const float2* stats;  // [B, ntiles] (mean, M2) of each kLnTile-column slice of x
+    int ntiles;
+    float eps;
+};
+
+// One weight matrix served by a GEMV launch (a launch serves one or two).
+struct GemvSeg {
+    const void* W;        // rows of `cols` elements
     UnitList list;        // which units
     int rpu;              // rows per unit
-    const float* y;       // [B, cols] fp32
-    int B;
-    int epi;
+    RowInput in;
     float* out;           // fp32 output
     int ld;               // leading dimension of out per batch row
+    int blocks;           // blocks of the launch serving this segment (set by the launcher)
+};
+
+struct GemvArgs {
+    GemvSeg seg[2];
+    int nseg;
+    int cols;             // row length in elements (d or r), shared by both segments
+    int B;
+    int epi;
     const void* bias;     // kEpiBiasRelu: per-unit bias (weight dtype)
     // kEpiQkv: cache [B, h, n_cap, dh]
     void* Kc;
@@ -174,12 +216,14 @@ struct AxpyArgs {
     int rows_per_chunk;
     const float* resid;   // may be nullptr
     float* out;           // [B, cols]
+    float2* stats;        // [B, ceil(cols / kLnTile)] (mean, M2) of each slice of out, or nullptr
     unsigned* flags;
     int prof;
 };
 
 hipError_t launch_axpy(bool f16, const AxpyArgs& a, hipStream_t s);
 int axpy_chunks(int rows_cap, int cols, bool f16, int* rows_per_chunk);
+constexpr int kAxpyMaxChunkRows = 1024;
 
 struct AttnArgs {
     const void* Kc;       // [B, h, n_cap, dh]
@@ -198,6 +242,7 @@ struct AttnArgs {
 
 hipError_t launch_attention(bool f16, const AttnArgs& a, hipStream_t s);
 int attn_chunk_for(bool f16, int dh);  // positions per attention chunk
+constexpr int kAttnMaxChunks = 1024;   // chunks per head the merge kernel accepts
 
 struct SelectJob {
     const float* z;       // [B, n_out]
@@ -213,6 +258,8 @@ struct SelectJob {
 hipError_t launch_select(const SelectJob* jobs, int njobs, int B, hipStream_t s, int prof);
 
 hipError_t launch_layernorm(int B, int d, const float* x, float* y, float eps, hipStream_t s);
+// (mean, M2) of each kLnTile-column slice of x [B, d].
+hipError_t launch_ln_stats(int B, int d, const float* x, float2* stats, hipStream_t s);
 
 unsigned* device_flags();  // this device's flag word (device address), nullptr on error
 

@@ -9,18 +9,10 @@ __device__ unsigned g_flags = 0u;
 namespace {
 
 constexpr int kLnThreads = 1024;
+constexpr int kLnPerThread = 16;   // d <= 16384 held in registers
 
-__device__ __forceinline__ float block_sum(float v, float* red) {
-    v = wave_sum(v);
-    if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = v;
-    __syncthreads();
-    float s = 0.f;
-    for (int q = 0; q < kLnThreads / kWave; ++q) s += red[q];
-    __syncthreads();
-    return s;
-}
-
-// y = (x - mean) / sqrt(var + eps), biased variance, no affine; one block per row.
+// y = (x - mean) / sqrt(var + eps), biased variance, no affine; one block per row with
+// the row held in registers (one round trip to memory).
 // Pre-LN block input: [NOTES "LLM Contextually Sparse", third finding] (residual blocks
 // with a Norm); eps, gamma = 1 and beta = 0 as in OPT.
 __global__ __launch_bounds__(kLnThreads) void layernorm_kernel(int d, const float* x, float* y,
@@ -28,24 +20,56 @@ __global__ __launch_bounds__(kLnThreads) void layernorm_kernel(int d, const floa
     __shared__ float red[kLnThreads / kWave];
     const float* xr = x + (size_t)blockIdx.x * d;
     float* yr = y + (size_t)blockIdx.x * d;
+    float v[kLnPerThread];
     float s = 0.f;
-    for (int i = threadIdx.x; i < d; i += kLnThreads) s += xr[i];
-    const float mean = block_sum(s, red) / (float)d;
+#pragma unroll
+    for (int i = 0; i < kLnPerThread; ++i) {
+        const int c = threadIdx.x + i * kLnThreads;
+        v[i] = c < d ? xr[c] : 0.f;
+        s += v[i];
+    }
+    const float mean = block_sum<kLnThreads>(s, red) / (float)d;
     float q = 0.f;
-    for (int i = threadIdx.x; i < d; i += kLnThreads) {
-        const float t = xr[i] - mean;
+#pragma unroll
+    for (int i = 0; i < kLnPerThread; ++i) {
+        const int c = threadIdx.x + i * kLnThreads;
+        const float t = c < d ? v[i] - mean : 0.f;
         q = fmaf(t, t, q);
     }
-    const float var = block_sum(q, red) / (float)d;
+    const float var = block_sum<kLnThreads>(q, red) / (float)d;
     const float rstd = 1.0f / sqrtf(var + eps);
-    for (int i = threadIdx.x; i < d; i += kLnThreads) yr[i] = (xr[i] - mean) * rstd;
+#pragma unroll
+    for (int i = 0; i < kLnPerThread; ++i) {
+        const int c = threadIdx.x + i * kLnThreads;
+        if (c < d) yr[c] = (v[i] - mean) * rstd;
+    }
+}
+
+// (mean, M2) of each kLnTile-column slice of x; one wave per (slice, row b).  The
+// LayerNorm of x is applied from these by the consuming kernel.
+__global__ __launch_bounds__(kWave) void ln_stats_kernel(int d, const float* x, float2* stats) {
+    const int tile = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
+    const int c0 = tile * kLnTile, n = min(kLnTile, d - c0);
+    const float v = c < n ? x[(size_t)b * d + c0 + c] : 0.f;
+    const float mean = wave_sum(v) / (float)n;
+    const float dv = c < n ? v - mean : 0.f;
+    const float M2 = wave_sum(dv * dv);
+    if (c == 0) stats[(size_t)b * gridDim.x + tile] = make_float2(mean, M2);
 }
 
 }  // namespace
 
 hipError_t launch_layernorm(int B, int d, const float* x, float* y, float eps, hipStream_t s) {
     if (B <= 0) return hipSuccess;
+    if (d > kLnThreads * kLnPerThread) return hipErrorInvalidValue;
     hipLaunchKernelGGL(layernorm_kernel, dim3(B), dim3(kLnThreads), 0, s, d, x, y, eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_ln_stats(int B, int d, const float* x, float2* stats, hipStream_t s) {
+    if (B <= 0) return hipSuccess;
+    const int tiles = (d + kLnTile - 1) / kLnTile;
+    hipLaunchKernelGGL(ln_stats_kernel, dim3(tiles, B), dim3(kWave), 0, s, d, x, stats);
     return hipGetLastError();
 }
 

@@ -58,6 +58,8 @@ class Stack:
             dj.dejavu_stack_decode(self.m, self.desc, x, lookahead, False, tr, self.ws,
                                    torch.cuda.current_stream(), s_pred)
         torch.cuda.synchronize()
+        # no out-of-range index and no count above its list's capacity on the device
+        assert dj.dejavu_poll_device_error() == 0
         return x, {k: host(v) for k, v in t.items()}
 
 

@@ -20,8 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdejavu.so")
 
-SOURCES = ["api.cpp", "gemv.hip", "gemv_pred.hip", "gemv_mlp.hip", "gemv_qkv.hip", "axpy.hip",
-           "attn.hip", "select.hip", "misc.hip"]
+SOURCES = ["api.cpp", "gemv.hip", "gemv_f16.hip", "gemv_f16_side.hip", "gemv_f32.hip",
+           "gemv_f32_side.hip", "axpy.hip", "attn.hip", "select.hip", "misc.hip"]
 ARCH = "gfx950"
 
 

@@ -241,86 +241,121 @@ struct PredJob {
     const PredWs* w;
 };
 
+// GEMV segments of the layer's weight streams.
+GemvSeg seg_first(const PredJob& j, int r, const RowInput& in) {
+    GemvSeg S{};
+    S.W = j.P1; S.list = UnitList{nullptr, nullptr, r, r}; S.rpu = 1; S.in = in;
+    S.out = j.w->u; S.ld = r; S.epi = kEpiRelu;
+    return S;
+}
+GemvSeg seg_second(const PredJob& j) {
+    GemvSeg S{};
+    S.W = j.P2; S.list = UnitList{nullptr, nullptr, j.n_out, j.n_out}; S.rpu = 1;
+    S.in = plain_input(j.w->u); S.out = j.z; S.ld = j.n_out; S.epi = kEpiStore;
+    return S;
+}
+SelectJob select_job(const PredJob& j) {
+    return SelectJob{j.z, j.n_out, j.mode, j.k, j.mode == DJV_THRESHOLD ? tau_key(j.t) : 0u,
+                     j.w->bits, j.idx, j.count};
+}
+GemvSeg seg_qkv(const void* Wqkv, const UnitList& heads, int dh, const RowInput& in, float* q) {
+    GemvSeg S{};
+    S.W = Wqkv; S.list = heads; S.rpu = 3 * dh; S.in = in; S.out = q; S.ld = heads.cap * dh;
+    S.epi = kEpiQkv;
+    return S;
+}
+GemvSeg seg_up(const void* W1, const void* b1, const UnitList& neurons, const RowInput& in, float* a) {
+    GemvSeg S{};
+    S.W = W1; S.list = neurons; S.rpu = 1; S.in = in; S.out = a; S.ld = neurons.cap;
+    S.epi = kEpiBiasRelu; S.bias = b1;
+    return S;
+}
+
+GemvArgs gemv_args(int cols, int B, int prof) {
+    GemvArgs g{};
+    g.cols = cols; g.B = B; g.flags = device_flags(); g.prof = prof;
+    return g;
+}
+void add_seg(GemvArgs& g, const GemvSeg& S) { g.seg[g.nseg++] = S; }
+void add_side(GemvArgs& g, const SelectJob& J) { g.side[g.nside++] = J; }
+
 // One or two predictors reading the same input, in three launches: both first layers
 // (one GEMV launch), both second layers (one launch), both selections (one launch).
 djv_status run_predict(bool f16, int B, int d, int r, const RowInput& in, const PredJob* jobs,
                        int njobs, hipStream_t s) {
-    unsigned* flags = device_flags();
-    // both first layers in one launch, then both second layers, then both selections
-    GemvArgs g{};
-    g.nseg = njobs; g.cols = d; g.B = B; g.epi = kEpiRelu; g.flags = flags; g.prof = DJV_PROF_PRED_1;
-    for (int i = 0; i < njobs; ++i) {
-        GemvSeg& S = g.seg[i];
-        S.W = jobs[i].P1; S.list = UnitList{nullptr, nullptr, r, r}; S.rpu = 1; S.in = in;
-        S.out = jobs[i].w->u; S.ld = r;
-    }
+    GemvArgs g = gemv_args(d, B, DJV_PROF_PRED_1);
+    for (int i = 0; i < njobs; ++i) add_seg(g, seg_first(jobs[i], r, in));
     DJV_HIP(launch_gemv(f16, g, s));
-    g = GemvArgs{};
-    g.nseg = njobs; g.cols = r; g.B = B; g.epi = kEpiStore; g.flags = flags; g.prof = DJV_PROF_PRED_2;
-    for (int i = 0; i < njobs; ++i) {
-        GemvSeg& S = g.seg[i];
-        S.W = jobs[i].P2; S.list = UnitList{nullptr, nullptr, jobs[i].n_out, jobs[i].n_out};
-        S.rpu = 1; S.in = plain_input(jobs[i].w->u); S.out = jobs[i].z; S.ld = jobs[i].n_out;
-    }
+    g = gemv_args(r, B, DJV_PROF_PRED_2);
+    for (int i = 0; i < njobs; ++i) add_seg(g, seg_second(jobs[i]));
     DJV_HIP(launch_gemv(f16, g, s));
     SelectJob sj[2];
-    for (int i = 0; i < njobs; ++i) {
-        const PredJob& J = jobs[i];
-        sj[i] = SelectJob{J.z, J.n_out, J.mode, J.k, J.mode == DJV_THRESHOLD ? tau_key(J.t) : 0u,
-                          J.w->bits, J.idx, J.count};
-    }
+    for (int i = 0; i < njobs; ++i) sj[i] = select_job(jobs[i]);
     DJV_HIP(launch_select(sj, njobs, B, s, DJV_PROF_SELECT));
     return DJV_OK;
 }
 
+// Row-axpy over the kept W2 rows: out = resid + W2_S^T a.  stats (optional) receives the
+// tile statistics of out.
+djv_status run_down(bool f16, int B, int d, const void* W2, const UnitList& neurons,
+                    const float* resid, float* out, float2* stats, const MlpWs& w, hipStream_t s) {
+    AxpyArgs x{};
+    x.W = W2; x.cols = d; x.list = neurons; x.rpu = 1; x.coef = w.a; x.ldc = neurons.cap; x.B = B;
+    x.partial = w.partial; x.rows_per_chunk = w.rpc; x.resid = resid;
+    x.out = out; x.stats = stats; x.flags = device_flags(); x.prof = DJV_PROF_MLP_DOWN;
+    DJV_HIP(launch_axpy(f16, x, s));
+    return DJV_OK;
+}
+
 // out = resid + MLP_S(in): gather-GEMV over the kept W1 rows, then row-axpy over the kept
-// W2 rows.  stats (optional) receives the tile statistics of out.
+// W2 rows.
 djv_status run_mlp(bool f16, int B, int d, int N, const RowInput& in, const void* W1,
                    const void* b1, const void* W2, const int32_t* idx, const int32_t* count,
                    int cap, const float* resid, float* out, float2* stats, const MlpWs& w,
                    hipStream_t s) {
-    unsigned* flags = device_flags();
     const UnitList list{idx, count, cap, N};
-    GemvArgs g{};
-    g.nseg = 1; g.cols = d; g.B = B; g.epi = kEpiBiasRelu; g.bias = b1; g.flags = flags;
-    g.prof = DJV_PROF_MLP_UP;
-    g.seg[0].W = W1; g.seg[0].list = list; g.seg[0].rpu = 1; g.seg[0].in = in;
-    g.seg[0].out = w.a; g.seg[0].ld = cap;
+    GemvArgs g = gemv_args(d, B, DJV_PROF_MLP_UP);
+    add_seg(g, seg_up(W1, b1, list, in, w.a));
     DJV_HIP(launch_gemv(f16, g, s));
+    return run_down(f16, B, d, W2, list, resid, out, stats, w, s);
+}
+
+// Split-position attention over the kept heads and its merge (q from the QKV step).
+djv_status run_attend(bool f16, int B, int h, int dh, int n, int n_cap, void* Kc, void* Vc,
+                      const UnitList& heads, float scale, const MhaWs& w, hipStream_t s) {
+    AttnArgs at{};
+    at.Kc = Kc; at.Vc = Vc; at.list = heads; at.h = h; at.dh = dh; at.n = n; at.n_cap = n_cap;
+    at.B = B; at.q = w.q; at.scale = scale; at.part = w.part; at.chunk = w.chunk;
+    at.nchunk = (n + 1 + w.chunk - 1) / w.chunk; at.H = w.H; at.flags = device_flags();
+    at.prof = DJV_PROF_ATTN;
+    DJV_HIP(launch_attention(f16, at, s));
+    return DJV_OK;
+}
+
+// Row-axpy over the kept heads' W_O rows: out = resid + sum_i H_i W_i^O.
+djv_status run_oproj(bool f16, int B, int d, int dh, const void* Wo, const UnitList& heads,
+                     const float* resid, float* out, float2* stats, const MhaWs& w, hipStream_t s) {
     AxpyArgs x{};
-    x.W = W2; x.cols = d; x.list = list; x.rpu = 1; x.coef = w.a; x.ldc = cap; x.B = B;
-    x.partial = w.partial; x.rows_per_chunk = w.rpc; x.resid = resid;
-    x.out = out; x.stats = stats; x.flags = flags; x.prof = DJV_PROF_MLP_DOWN;
+    x.W = Wo; x.cols = d; x.list = heads; x.rpu = dh; x.coef = w.H; x.ldc = heads.cap * dh; x.B = B;
+    x.partial = w.partial; x.rows_per_chunk = w.rpc; x.resid = resid; x.out = out; x.stats = stats;
+    x.flags = device_flags(); x.prof = DJV_PROF_O_PROJ;
     DJV_HIP(launch_axpy(f16, x, s));
     return DJV_OK;
 }
 
 // out = resid + MHA_S(in), appending the kept heads' K/V at position n: head-sparse QKV
-// GEMV, split-position attention and its merge, row-axpy over the kept
-// heads' W_O rows.  stats (optional) receives the tile statistics of out.
+// GEMV, split-position attention and its merge, row-axpy over the kept heads' W_O rows.
 djv_status run_mha(bool f16, int B, int d, int h, int dh, int n, int n_cap, const RowInput& in,
                    const void* Wqkv, const void* Wo, void* Kc, void* Vc, const int32_t* idx,
                    const int32_t* count, int cap, float scale, const float* resid, float* out,
                    float2* stats, const MhaWs& w, hipStream_t s) {
-    unsigned* flags = device_flags();
-    const UnitList list{idx, count, cap, h};
-    GemvArgs g{};
-    g.nseg = 1; g.cols = d; g.B = B; g.epi = kEpiQkv; g.Kc = Kc; g.Vc = Vc; g.h = h; g.dh = dh;
-    g.n = n; g.n_cap = n_cap; g.flags = flags; g.prof = DJV_PROF_QKV;
-    g.seg[0].W = Wqkv; g.seg[0].list = list; g.seg[0].rpu = 3 * dh; g.seg[0].in = in;
-    g.seg[0].out = w.q; g.seg[0].ld = cap * dh;
+    const UnitList heads{idx, count, cap, h};
+    GemvArgs g = gemv_args(d, B, DJV_PROF_QKV);
+    g.Kc = Kc; g.Vc = Vc; g.h = h; g.dh = dh; g.n = n; g.n_cap = n_cap;
+    add_seg(g, seg_qkv(Wqkv, heads, dh, in, w.q));
     DJV_HIP(launch_gemv(f16, g, s));
-    AttnArgs at{};
-    at.Kc = Kc; at.Vc = Vc; at.list = list; at.h = h; at.dh = dh; at.n = n; at.n_cap = n_cap;
-    at.B = B; at.q = w.q; at.scale = scale; at.part = w.part; at.chunk = w.chunk;
-    at.nchunk = (n + 1 + w.chunk - 1) / w.chunk; at.H = w.H; at.flags = flags;
-    at.prof = DJV_PROF_ATTN;
-    DJV_HIP(launch_attention(f16, at, s));
-    AxpyArgs x{};
-    x.W = Wo; x.cols = d; x.list = list; x.rpu = dh; x.coef = w.H; x.ldc = cap * dh; x.B = B;
-    x.partial = w.partial; x.rows_per_chunk = w.rpc; x.resid = resid; x.out = out; x.stats = stats; x.flags = flags; x.prof = DJV_PROF_O_PROJ;
-    DJV_HIP(launch_axpy(f16, x, s));
-    return DJV_OK;
+    DJV_TRY(run_attend(f16, B, h, dh, n, n_cap, Kc, Vc, heads, scale, w, s));
+    return run_oproj(f16, B, d, dh, Wo, heads, resid, out, stats, w, s);
 }
 
 djv_status check_model(const djv_model* m) {
@@ -675,14 +710,14 @@ djv_status dejavu_sparse_layer(const djv_model* m, const djv_layer* layer, float
 
 djv_status dejavu_stack_decode(const djv_model* m, const djv_layer* layers, int L, float* x,
                                int lookahead, int dense, const djv_trace* trace, void* ws,
-                               size_t ws_bytes, void* s_main, void* s_pred) {
+                               size_t ws_bytes, void* stream) {
     DJV_TRY(check_model(m));
     DJV_REQUIRE(L >= 1, DJV_EINVAL, "L must be >= 1");
     DJV_REQUIRE(layers != nullptr, DJV_EINVAL, "layers is NULL");
     for (int l = 0; l < L; ++l) DJV_TRY(check_layer(&layers[l], dense != 0));
     DJV_TRY(check_ptr(x, "x"));
     DJV_TRY(check_ws(ws, ws_bytes, layer_ws_bytes(*m)));
-    hipStream_t sm = (hipStream_t)s_main, sp = (hipStream_t)s_pred;
+    hipStream_t sm = (hipStream_t)stream;
     const bool f16 = m->wt == DJV_F16;
     Arena A(ws);
     const LayerWs w = plan_layer(A, *m, dense != 0);
@@ -711,40 +746,74 @@ djv_status dejavu_stack_decode(const djv_model* m, const djv_layer* layers, int 
         return DJV_OK;
     }
 
-    // Lookahead schedule: S^{l+1} from LN(x_l) on the predictor stream while layer l runs.
-    hipEvent_t evY = nullptr, evS = nullptr;
-    DJV_HIP(hipEventCreateWithFlags(&evY, hipEventDisableTiming));
-    if (hipEventCreateWithFlags(&evS, hipEventDisableTiming) != hipSuccess) {
-        (void)hipEventDestroy(evY);
-        return fail(DJV_EHIP, "hipEventCreateWithFlags failed");
-    }
-    struct Guard {
-        hipEvent_t a, b;
-        ~Guard() { (void)hipEventDestroy(a); (void)hipEventDestroy(b); }
-    } guard{evY, evS};
-
+    // Lookahead schedule on one stream: the sets of layer l+1 are predicted from LN(x_l)
+    // inside layer l's launches.  Both first predictor layers share the Q/K/V launch (same
+    // input), the second layers run after the attention, and each selection runs in a side
+    // block of a later weight stream: S_A^{l+1} beside the MLP up-projection of layer l,
+    // S_M^l beside the Q/K/V launch of layer l.
+    const int capA = cap_of(m->mode, m->k_A, m->h, m->B), capM = cap_of(m->mode, m->k_M, m->N, m->B);
     {
-        // layer 0's sets, serially from LN(x_0)
+        // layer 0's scores from LN(x_0); S_A^0 alone, S_M^0 in layer 0's Q/K/V launch
         const LayerIO io0 = layer_io(x, w, 0, L);
-        const PredJob j2[2] = {job_A(*m, layers[0], w, 0, trace, 0), job_M(*m, layers[0], w, 0, trace, 0)};
-        DJV_TRY(run_predict(f16, m->B, m->d, m->r, ln_input(io0.x_in, io0.s_in, w, m->eps), j2, 2, sm));
+        const RowInput in0 = ln_input(io0.x_in, io0.s_in, w, m->eps);
+        const PredJob ja = job_A(*m, layers[0], w, 0, trace, 0), jm = job_M(*m, layers[0], w, 0, trace, 0);
+        GemvArgs g = gemv_args(m->d, m->B, DJV_PROF_PRED_1);
+        add_seg(g, seg_first(ja, m->r, in0));
+        add_seg(g, seg_first(jm, m->r, in0));
+        DJV_HIP(launch_gemv(f16, g, sm));
+        g = gemv_args(m->r, m->B, DJV_PROF_PRED_2);
+        add_seg(g, seg_second(ja));
+        add_seg(g, seg_second(jm));
+        DJV_HIP(launch_gemv(f16, g, sm));
+        const SelectJob sa = select_job(ja);
+        DJV_HIP(launch_select(&sa, 1, m->B, sm, DJV_PROF_SELECT));
     }
-    DJV_HIP(hipEventRecord(evY, sm));
     for (int l = 0; l < L; ++l) {
         const int cur = l & 1, nxt = (l + 1) & 1;
+        const bool ahead = l + 1 < L;
+        const djv_layer& Ly = layers[l];
         const LayerIO io = layer_io(x, w, l, L);
-        if (l >= 1) DJV_HIP(hipStreamWaitEvent(sm, evS, 0));  // S^l ready
-        DJV_TRY(trace_x(trace, *m, l, io.x_in, sm));
-        DJV_TRY(trace_sets(trace, *m, l, w, cur, sm));
-        if (l + 1 < L) {
-            DJV_HIP(hipStreamWaitEvent(sp, evY, 0));           // x_l ready, buffer nxt free
-            const PredJob j2[2] = {job_A(*m, layers[l + 1], w, nxt, trace, l + 1),
-                                   job_M(*m, layers[l + 1], w, nxt, trace, l + 1)};
-            DJV_TRY(run_predict(f16, m->B, m->d, m->r, ln_input(io.x_in, io.s_in, w, m->eps), j2, 2, sp));
-            DJV_HIP(hipEventRecord(evS, sp));
+        const RowInput in_a = ln_input(io.x_in, io.s_in, w, m->eps);
+        const UnitList heads{w.idxA[cur], count_of(*m, w.cntA[cur]), capA, m->h};
+        const UnitList neurons{w.idxM[cur], count_of(*m, w.cntM[cur]), capM, m->N};
+        PredJob na{}, nm{};
+        if (ahead) {
+            na = job_A(*m, layers[l + 1], w, nxt, trace, l + 1);
+            nm = job_M(*m, layers[l + 1], w, nxt, trace, l + 1);
         }
-        DJV_TRY(layer_body(*m, layers[l], io, w, cur, false, trace, l, sm));
-        if (l + 1 < L) DJV_HIP(hipEventRecord(evY, sm));
+        DJV_TRY(trace_x(trace, *m, l, io.x_in, sm));
+
+        // Q/K/V of the kept heads (+ K/V append), P1 of both predictors for l+1, S_M^l
+        GemvArgs g = gemv_args(m->d, m->B, DJV_PROF_QKV);
+        g.Kc = Ly.Kc; g.Vc = Ly.Vc; g.h = m->h; g.dh = m->dh; g.n = m->n; g.n_cap = m->n_cap;
+        add_seg(g, seg_qkv(Ly.Wqkv, heads, m->dh, in_a, w.mha.q));
+        if (ahead) {
+            add_seg(g, seg_first(na, m->r, in_a));
+            add_seg(g, seg_first(nm, m->r, in_a));
+        }
+        add_side(g, select_job(job_M(*m, Ly, w, cur, trace, l)));
+        DJV_HIP(launch_gemv(f16, g, sm));
+        DJV_TRY(trace_sets(trace, *m, l, w, cur, sm));
+
+        DJV_TRY(run_attend(f16, m->B, m->h, m->dh, m->n, m->n_cap, Ly.Kc, Ly.Vc, heads, m->scale,
+                           w.mha, sm));
+        if (ahead) {
+            // P2 of both predictors for l+1
+            g = gemv_args(m->r, m->B, DJV_PROF_PRED_2);
+            add_seg(g, seg_second(na));
+            add_seg(g, seg_second(nm));
+            DJV_HIP(launch_gemv(f16, g, sm));
+        }
+        DJV_TRY(run_oproj(f16, m->B, m->d, m->dh, Ly.Wo, heads, io.x_in, w.xm, w.sm, w.mha, sm));
+        if (trace && trace->x_mid)
+            DJV_TRY(copy_async(trace->x_mid + (size_t)l * m->B * m->d, w.xm, (size_t)m->B * m->d * 4, sm));
+
+        // MLP up-projection of the kept neurons, S_A^{l+1}
+        g = gemv_args(m->d, m->B, DJV_PROF_MLP_UP);
+        add_seg(g, seg_up(Ly.W1, Ly.b1, neurons, ln_input(w.xm, w.sm, w, m->eps), w.mlp.a));
+        if (ahead) add_side(g, select_job(na));
+        DJV_HIP(launch_gemv(f16, g, sm));
+        DJV_TRY(run_down(f16, m->B, m->d, Ly.W2, neurons, w.xm, io.x_out, io.s_out, w.mlp, sm));
     }
     return DJV_OK;
 }

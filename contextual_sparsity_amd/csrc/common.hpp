@@ -43,6 +43,25 @@ __device__ __forceinline__ Vec16 ldg16_nt(const void* p) {
     return v;
 }
 
+// A global-memory pointer known to be the same in every lane of the wave, moved to
+// scalar registers: a 16-byte load through it at a 32-bit per-lane offset takes the
+// scalar-base form (one vector register per offset, no 64-bit address arithmetic).
+typedef const __attribute__((address_space(1))) char gchar;
+__device__ __forceinline__ gchar* uniform_ptr(const void* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<gchar*>(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ Vec16 ldg16_nt_at(gchar* base, uint32_t off) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    typedef const __attribute__((address_space(1))) u32x4 gu32x4;
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<gu32x4*>(base + off));
+    Vec16 v;
+    v.w[0] = t[0]; v.w[1] = t[1]; v.w[2] = t[2]; v.w[3] = t[3];
+    return v;
+}
+
 __device__ __forceinline__ float lo_h(uint32_t u) {
     return __half2float(__ushort_as_half((unsigned short)(u & 0xffffu)));
 }
@@ -141,6 +160,35 @@ __device__ __forceinline__ int read_count(const UnitList& L, unsigned* flags) {
     return c;
 }
 
+// Scalar (wave-uniform) load of an int through the constant address space: the value
+// lands in a scalar register and the wait for it does not also wait for the vector loads
+// in flight.  Only for addresses uniform over the wave, in memory the running kernel does
+// not write.
+typedef const __attribute__((address_space(4))) int32_t cint32_k;
+typedef const __attribute__((address_space(4))) uint32_t cuint32_k;
+__device__ __forceinline__ int32_t sload_i32(const int32_t* p) { return *(cint32_k*)p; }
+__device__ __forceinline__ uint32_t sload_u32(const void* p) { return *(cuint32_k*)p; }
+
+__device__ __forceinline__ int read_count_uniform(const UnitList& L, unsigned* flags) {
+    if (!L.count) return L.cap;
+    int c = sload_i32(L.count);
+    if (c < 0 || c > L.cap) {
+        set_flag(flags, kFlagBadCount);
+        c = c < 0 ? 0 : L.cap;
+    }
+    return c;
+}
+
+__device__ __forceinline__ int unit_of_uniform(const UnitList& L, int u, unsigned* flags) {
+    if (!L.idx) return u;
+    const int j = sload_i32(L.idx + u);
+    if (j < 0 || j >= L.units) {
+        set_flag(flags, kFlagBadIndex);
+        return -1;
+    }
+    return j;
+}
+
 // Returns the unit of slot u or -1 (and flags it) when the index is out of range.
 __device__ __forceinline__ int unit_of(const UnitList& L, int u, unsigned* flags) {
     if (!L.idx) return u;
@@ -176,7 +224,19 @@ struct RowInput {
     float eps;
 };
 
-// One weight matrix served by a GEMV launch (a launch serves one or two).
+struct SelectJob {
+    const float* z;       // [B, n_out]
+    int n_out;
+    int mode;             // 0 top-k, 1 threshold
+    int k;
+    uint32_t tau_key;     // threshold in the order-preserving key space
+    uint32_t* bits;       // [B, words] per-row selection bitmaps (workspace; parallel rows only)
+    int32_t* idx;         // [n_out]
+    int32_t* count;       // [1]
+};
+
+// One weight matrix served by a GEMV launch (a launch serves up to three, all with rows
+// of the same length and the same kind of input).
 struct GemvSeg {
     const void* W;        // rows of `cols` elements
     UnitList list;        // which units
@@ -184,20 +244,27 @@ struct GemvSeg {
     RowInput in;
     float* out;           // fp32 output
     int ld;               // leading dimension of out per batch row
+    int epi;              // GemvEpi of this segment
+    const void* bias;     // kEpiBiasRelu: per-unit bias (weight dtype)
     int blocks;           // blocks of the launch serving this segment (set by the launcher)
 };
 
+constexpr int kMaxSeg = 3;
+constexpr int kMaxSide = 2;
+
 struct GemvArgs {
-    GemvSeg seg[2];
+    GemvSeg seg[kMaxSeg];
     int nseg;
-    int cols;             // row length in elements (d or r), shared by both segments
+    int cols;             // row length in elements (d or r), shared by all segments
     int B;
-    int epi;
-    const void* bias;     // kEpiBiasRelu: per-unit bias (weight dtype)
     // kEpiQkv: cache [B, h, n_cap, dh]
     void* Kc;
     void* Vc;
     int h, dh, n, n_cap;
+    // selections run by the first nside blocks of the launch, each over all B rows of its
+    // scores (union in the block), independent of the GEMV segments
+    SelectJob side[kMaxSide];
+    int nside;
     unsigned* flags;
     int prof;             // profiling family of this launch (0: none)
 };
@@ -244,17 +311,6 @@ hipError_t launch_attention(bool f16, const AttnArgs& a, hipStream_t s);
 int attn_chunk_for(bool f16, int dh);  // positions per attention chunk
 constexpr int kAttnMaxChunks = 1024;   // chunks per head the merge kernel accepts
 
-struct SelectJob {
-    const float* z;       // [B, n_out]
-    int n_out;
-    int mode;             // 0 top-k, 1 threshold
-    int k;
-    uint32_t tau_key;     // threshold in the order-preserving key space
-    uint32_t* bits;       // [B, words] per-row selection bitmaps (workspace)
-    int32_t* idx;         // [n_out]
-    int32_t* count;       // [1]
-};
-
 hipError_t launch_select(const SelectJob* jobs, int njobs, int B, hipStream_t s, int prof);
 
 hipError_t launch_layernorm(int B, int d, const float* x, float* y, float eps, hipStream_t s);
@@ -262,6 +318,7 @@ hipError_t launch_layernorm(int B, int d, const float* x, float* y, float eps, h
 hipError_t launch_ln_stats(int B, int d, const float* x, float2* stats, hipStream_t s);
 
 unsigned* device_flags();  // this device's flag word (device address), nullptr on error
+int device_cus();          // compute units of the current device
 
 // Benchmark hook: events recorded around the launches of one kernel family.
 struct ProfHook {

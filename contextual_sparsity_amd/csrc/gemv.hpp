@@ -8,22 +8,31 @@
 //   names coalescing without detail; here every kept unit is one or more contiguous
 //   rows, so each wave reads contiguous 1 KiB spans with 16-byte loads.
 //
-// Work decomposition (gfx950, wave64, 256-thread blocks):
-//   * A "team" of TS threads (64 = one wave, or 256 = the whole block) owns one row at a
+// Work decomposition (gfx950, wave64, 1024-thread blocks):
+//   * A "team" of TS threads (64 = one wave, or 256 = four waves) owns one row at a
 //     time; thread t of the team owns the 16-byte vectors t, t+TS, t+2TS, ... of every
 //     row, so its slice of y is the same for all rows and stays in registers.
 //   * A team processes G rows together: G*NV independent 16-byte loads are in flight per
-//     thread before any arithmetic, which is what keeps HBM busy.
+//     thread before any arithmetic, and the next group's loads go out before the current
+//     group is reduced, which is what keeps HBM busy.
+//   * The grid is persistent: as many blocks as the device holds at once (all resident,
+//     so none waits for another to finish), and team t of block b takes the groups
+//     b*NT + t, b*NT + t + blocks*NT, ...; every block loads its y slice once.
 //   * Dot products: fp32 weights use fp32 FMA; fp16 weights use v_dot2_f32_f16 with y
 //     packed to fp16 pairs (fp32 accumulation).
 //   * Team reduction: wave butterfly, then (TS = 256) a 4-entry LDS combine.
 //   * The activation rows are either given, or LayerNorm(x) is applied while the slice is
 //     loaded, from per-slice (mean, M2) statistics written by the kernel that produced x,
 //     so no separate normalisation pass runs.
-//   * One launch may serve two weight matrices of the same row length (the head and the
-//     neuron predictor): blocks [0, seg[0].blocks) serve the first, the rest the second.
+//   * One launch may serve up to three weight matrices of the same row length and input
+//     (e.g. the kept heads' Q/K/V rows and both predictors' first layers, which all read
+//     LN(x)), each with its own epilogue; the grid is shared in proportion to their rows.
+//   * The first blocks of a launch may instead run a selection (one block over all batch
+//     rows of a score vector), so a selection overlaps a long weight stream rather than
+//     running alone on one compute unit.
 #pragma once
 #include "common.hpp"
+#include "select.hpp"
 
 namespace djv {
 namespace gemv_detail {
@@ -101,46 +110,29 @@ __device__ __forceinline__ void row_moments(const RowInput& in, int cols, int b,
     rstd = 1.0f / sqrtf(wave_sum(qs) / (float)cols + in.eps);
 }
 
-// Resolve visited row r to (unit slot, unit, weight row); row < 0 when skipped.
-struct RowRef {
-    int u, unit, sub;
-    long long row;
-};
-
-__device__ __forceinline__ RowRef resolve(const GemvSeg& S, int r, unsigned* flags) {
-    RowRef rr;
-    rr.u = r / S.rpu;
-    rr.sub = r - rr.u * S.rpu;
-    rr.unit = unit_of(S.list, rr.u, flags);
-    rr.row = rr.unit < 0 ? -1 : (long long)rr.unit * S.rpu + rr.sub;
-    return rr;
-}
-
-template <typename T, int EPI>
-__device__ __forceinline__ void epilogue(const GemvArgs& a, const GemvSeg& S, int r, int b, float acc) {
-    const RowRef rr = resolve(S, r, a.flags);
-    switch (EPI) {
+// Writes the result of visited row r (weight unit `unit`, -1 when skipped) for batch row b.
+template <typename T>
+__device__ __forceinline__ void epilogue(const GemvArgs& a, const GemvSeg& S, int r, int b, float acc,
+                                         int unit, float bias) {
+    switch (S.epi) {
     case kEpiStore:
         S.out[(size_t)b * S.ld + r] = acc;
         break;
     case kEpiRelu:
         S.out[(size_t)b * S.ld + r] = fmaxf(acc, 0.f);
         break;
-    case kEpiBiasRelu: {
-        float v = 0.f;
-        if (rr.unit >= 0)
-            v = fmaxf(acc + to_f32<T>(reinterpret_cast<const T*>(a.bias)[rr.unit]), 0.f);
-        S.out[(size_t)b * S.ld + rr.u] = v;
+    case kEpiBiasRelu:
+        S.out[(size_t)b * S.ld + r] = unit >= 0 ? fmaxf(acc + bias, 0.f) : 0.f;
         break;
-    }
     case kEpiQkv: {
-        if (rr.unit < 0) break;
-        const int part = rr.sub / a.dh, c = rr.sub - part * a.dh;
+        if (unit < 0) break;
+        const int u = r / S.rpu, sub = r - u * S.rpu;
+        const int part = sub / a.dh, c = sub - part * a.dh;
         if (part == 0) {
-            S.out[((size_t)b * S.list.cap + rr.u) * a.dh + c] = acc;
+            S.out[((size_t)b * S.list.cap + u) * a.dh + c] = acc;
         } else {
             T* cache = reinterpret_cast<T*>(part == 1 ? a.Kc : a.Vc);
-            cache[(((size_t)b * a.h + rr.unit) * a.n_cap + a.n) * a.dh + c] = to_store<T>(acc);
+            cache[(((size_t)b * a.h + unit) * a.n_cap + a.n) * a.dh + c] = to_store<T>(acc);
         }
         break;
     }
@@ -149,197 +141,322 @@ __device__ __forceinline__ void epilogue(const GemvArgs& a, const GemvSeg& S, in
     }
 }
 
-template <typename T, int TS, int NV, int NB, int G, int EPI>
-__global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
+// Per-unit bias of kEpiBiasRelu, read with a scalar load of its aligned 32-bit word.
+template <typename T>
+__device__ __forceinline__ float load_bias(const void* bias, int unit);
+template <>
+__device__ __forceinline__ float load_bias<float>(const void* bias, int unit) {
+    return __uint_as_float(sload_u32(reinterpret_cast<const float*>(bias) + unit));
+}
+template <>
+__device__ __forceinline__ float load_bias<__half>(const void* bias, int unit) {
+    const uint32_t w = sload_u32(reinterpret_cast<const __half*>(bias) + (unit & ~1));
+    return (unit & 1) ? hi_h(w) : lo_h(w);
+}
+
+// Block sizes: launches that carry side selections use 1024-thread blocks (a selection
+// block needs them); the others use 256-thread blocks, which the hardware schedules with
+// less coupling between teams.
+constexpr int kSideThreads = 1024;
+constexpr int kPlainThreads = 256;
+template <bool SIDE> struct BlockOf { static constexpr int value = SIDE ? kSideThreads : kPlainThreads; };
+
+// A row of zeros as long as the longest supported row: a group slot with no row (past
+// the end of the list, or a skipped unit) loads from here, so every load is issued
+// unconditionally and the weight buffers keep fixed registers across loop trips.
+static __device__ const Vec16 g_zero_row[2048] = {};
+
+// Weights of one group of G rows in flight, with the rows' units and biases (scalar).
+template <int G, int NV>
+struct Group {
+    Vec16 w[G][NV];
+    int unit[G];
+    float bias[G];
+};
+
+template <typename T, int TS, int NV, int NB, int G, bool SIDE>
+__global__ __launch_bounds__(BlockOf<SIDE>::value) void gemv_kernel(GemvArgs a) {
+    constexpr int kThreads = BlockOf<SIDE>::value;
+    if constexpr (SIDE) {
+        if ((int)blockIdx.x < a.nside) {
+            __shared__ sel::RowShared SS;
+            sel::select_union_block(SS, a.side[blockIdx.x], a.B);
+            return;
+        }
+    }
     constexpr int E = WTraits<T>::kPerVec;
-    constexpr int NT = 256 / TS;
+    constexpr int NT = kThreads / TS;
     constexpr int NW = TS / kWave;  // waves per team
-    __shared__ float red[4][G * NB];
+    __shared__ float red[2][NT][NW][G * NB];
 
     const int tid = threadIdx.x;
-    const int tm = tid / TS, lt = tid % TS, wv = lt / kWave, ln = tid % kWave;
-    const int sg = (a.nseg > 1 && (int)blockIdx.x >= a.seg[0].blocks) ? 1 : 0;
+    // a team is whole waves, so its index, and with it every row, unit and row address,
+    // is uniform over the wave and lives in scalar registers
+    const int tm = __builtin_amdgcn_readfirstlane(tid / TS);
+    const int lt = tid % TS, wv = lt / kWave, ln = tid % kWave;
+    int bid = (int)blockIdx.x - (SIDE ? a.nside : 0);
+    int sg = 0;
+#pragma unroll
+    for (int i = 0; i + 1 < kMaxSeg; ++i)
+        if (sg == i && i + 1 < a.nseg && bid >= a.seg[i].blocks) {
+            bid -= a.seg[i].blocks;
+            sg = i + 1;
+        }
     const GemvSeg S = a.seg[sg];
-    const int bid = (int)blockIdx.x - (sg ? a.seg[0].blocks : 0);
     const int nvec = a.cols / E;
-    const int count = read_count(S.list, a.flags);
+    const int count = read_count_uniform(S.list, a.flags);
     const int rows = count * S.rpu;
     const int groups = (rows + G - 1) / G;
+    const int stride = S.blocks * NT;  // groups between a team's consecutive groups
     const char* Wb = reinterpret_cast<const char*>(S.W);
     const size_t row_bytes = (size_t)a.cols * sizeof(T);
+    const bool with_bias = S.epi == kEpiBiasRelu;
 
-    // all rows of a group are resolved (index loads) before any weight load is issued, so
-    // one round trip covers the indices and one the weights
-    auto load_group = [&](Vec16 (&w)[G][NV], int grp) {
-        long long row[G];
+    // units (and biases) come from scalar loads and row addresses are scalar, so the
+    // weight loads of a group depend on no vector load (nothing waits for the other
+    // group's weights in flight).  Vector i of a row sits at scalar base row + 16*TS*i
+    // and lane offset 16*lt; only the last vector can pass the row end (when the row is
+    // not a whole number of team widths), and there a lane reads the row's last vector
+    // instead: its activation is zero, so it adds 0 (weights are finite).
+    const uint32_t lane_off = (uint32_t)lt * 16u;
+    const uint32_t last_off = (uint32_t)(min(lt + TS * (NV - 1), nvec - 1) - TS * (NV - 1)) * 16u;
+    gchar* zero_row = uniform_ptr(g_zero_row);
+    auto load_group = [&](Group<G, NV>& q, int grp) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const int r = grp * G + g;
-            row[g] = r < rows ? resolve(S, r, a.flags).row : -1;
+            int unit = -1;
+            if (r < rows) unit = unit_of_uniform(S.list, r / S.rpu, a.flags);
+            q.unit[g] = unit;
+            q.bias[g] = (with_bias && unit >= 0) ? load_bias<T>(S.bias, unit) : 0.f;
         }
 #pragma unroll
-        for (int g = 0; g < G; ++g)
+        for (int g = 0; g < G; ++g) {
+            const int r = grp * G + g;
+            const int u = r / S.rpu;
+            const size_t row = (size_t)(q.unit[g] < 0 ? 0 : q.unit[g]) * S.rpu + (r - u * S.rpu);
+            gchar* rp = q.unit[g] < 0 ? zero_row : uniform_ptr(Wb + row * row_bytes);
 #pragma unroll
-            for (int i = 0; i < NV; ++i) {
-                const int v = lt + TS * i;
-                if (row[g] >= 0 && v < nvec)
-                    w[g][i] = ldg16_nt(Wb + (size_t)row[g] * row_bytes + (size_t)v * 16);
-                else
-                    w[g][i] = Vec16{{0u, 0u, 0u, 0u}};
-            }
+            for (int i = 0; i < NV; ++i)
+                q.w[g][i] = ldg16_nt_at(rp + (size_t)16 * TS * i, i + 1 < NV ? lane_off : last_off);
+        }
     };
 
-    // the first group's weights are requested before the activation slice is read
-    int grp = bid * NT + tm;
-    Vec16 w[G][NV];
-    if (grp < groups) load_group(w, grp);
+    // the first group's weights are requested before the activation slice is read, the
+    // second group's right after it; from then on two groups per team are in flight
+    const int base0 = bid * NT;
+    if (base0 >= groups) return;  // uniform over the block
+    Group<G, NV> qa, qb;
+    load_group(qa, base0 + tm);
 
     // this thread's slice of every batch row (loads clamped in range, then masked)
-    float raw[NB][NV][8];
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int v = min(lt + TS * i, nvec - 1);
-            load_raw<T>(S.in, a.cols, min(b, a.B - 1), v * E, raw[b][i]);
-        }
     YSlice<T> ys[NB][NV];
+    {
+        float raw[NB][NV][8];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-        float mean = 0.f, rstd = 1.f;
-        if (!S.in.y) row_moments(S.in, a.cols, min(b, a.B - 1), mean, rstd);
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const bool ok = b < a.B && lt + TS * i < nvec;
+            for (int i = 0; i < NV; ++i) {
+                const int v = min(lt + TS * i, nvec - 1);
+                load_raw<T>(S.in, a.cols, min(b, a.B - 1), v * E, raw[b][i]);
+            }
 #pragma unroll
-            for (int e = 0; e < E; ++e) raw[b][i][e] = ok ? (raw[b][i][e] - mean) * rstd : 0.f;
-            ys[b][i].set(raw[b][i], 0);
+        for (int b = 0; b < NB; ++b) {
+            float mean = 0.f, rstd = 1.f;
+            if (!S.in.y) row_moments(S.in, a.cols, min(b, a.B - 1), mean, rstd);
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const bool ok = b < a.B && lt + TS * i < nvec;
+#pragma unroll
+                for (int e = 0; e < E; ++e) raw[b][i][e] = ok ? (raw[b][i][e] - mean) * rstd : 0.f;
+                ys[b][i].set(raw[b][i], 0);
+            }
         }
     }
+    load_group(qb, base0 + stride + tm);
 
-    while (grp < groups) {
+    // One group: dot products on q, then q is refilled with the group two steps ahead
+    // before the reduction.  Every team of the block runs the same number of steps (a
+    // team past the end computes on stale registers and stores nothing), so the block
+    // barriers stay uniform.
+    auto step = [&](Group<G, NV>& q, int base, int parity) {
+        const int cur = base + tm;
         float acc[G][NB];
+        int unit[G];
+        float bias[G];
 #pragma unroll
-        for (int g = 0; g < G; ++g)
+        for (int g = 0; g < G; ++g) {
+            unit[g] = q.unit[g];
+            bias[g] = q.bias[g];
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 float s = 0.f;
 #pragma unroll
-                for (int i = 0; i < NV; ++i) s = ys[b][i].dot(w[g][i], s);
+                for (int i = 0; i < NV; ++i) s = ys[b][i].dot(q.w[g][i], s);
                 acc[g][b] = s;
             }
-        // the next group's loads go out before this group's reduction
-        const int cur = grp;
-        grp += S.blocks * NT;
-        if (grp < groups) load_group(w, grp);
+        }
+        load_group(q, cur + 2 * stride);
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
             for (int b = 0; b < NB; ++b) acc[g][b] = wave_sum(acc[g][b]);
         if constexpr (NW == 1) {
-            if (ln < G * NB) {
+            if (ln < G * NB && cur < groups) {
                 // lane j of the wave writes result j (all lanes hold every sum)
-                float v = 0.f;
+                float v = 0.f, bs = 0.f;
+                int un = -1;
 #pragma unroll
                 for (int g = 0; g < G; ++g)
 #pragma unroll
                     for (int b = 0; b < NB; ++b)
-                        if (ln == g * NB + b) v = acc[g][b];
+                        if (ln == g * NB + b) {
+                            v = acc[g][b];
+                            un = unit[g];
+                            bs = bias[g];
+                        }
                 const int g = ln / NB, b = ln % NB;
                 const int r = cur * G + g;
-                if (r < rows && b < a.B) epilogue<T, EPI>(a, S, r, b, v);
+                if (r < rows && b < a.B) epilogue<T>(a, S, r, b, v, un, bs);
             }
         } else {
+            // wave sums through LDS, double-buffered so one barrier per group suffices
+            float (&rb)[NT][NW][G * NB] = red[parity];
             if (ln == 0) {
 #pragma unroll
                 for (int g = 0; g < G; ++g)
 #pragma unroll
-                    for (int b = 0; b < NB; ++b) red[wv][g * NB + b] = acc[g][b];
+                    for (int b = 0; b < NB; ++b) rb[tm][wv][g * NB + b] = acc[g][b];
             }
             __syncthreads();
-            if (tid < G * NB) {
+            if (lt < G * NB && cur < groups) {
                 float v = 0.f;
 #pragma unroll
-                for (int q = 0; q < NW; ++q) v += red[q][tid];
-                const int g = tid / NB, b = tid % NB;
+                for (int w = 0; w < NW; ++w) v += rb[tm][w][lt];
+                float bs = 0.f;
+                int un = -1;
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    if (lt / NB == g) {
+                        un = unit[g];
+                        bs = bias[g];
+                    }
+                const int g = lt / NB, b = lt % NB;
                 const int r = cur * G + g;
-                if (r < rows && b < a.B) epilogue<T, EPI>(a, S, r, b, v);
+                if (r < rows && b < a.B) epilogue<T>(a, S, r, b, v, un, bs);
             }
-            __syncthreads();
         }
+    };
+    // both buffers are stepped every trip (the second step of the last trip may have no
+    // group for any team and then only computes on stale registers), so the loop has one
+    // exit and the buffers keep their registers across trips: no copy of a buffer whose
+    // loads are still in flight
+    for (int base = base0; base < groups; base += 2 * stride) {
+        step(qa, base, 0);
+        step(qb, base + stride, 1);
     }
 }
 
-template <typename T, int TS, int NB, int EPI>
-hipError_t dispatch_nv(const GemvArgs& a, int nv, dim3 grid, hipStream_t s) {
-#define DJV_GEMV_CASE(NVV, GG)                                                                 \
-    case NVV:                                                                                  \
-        prof_begin(a.prof, s);                                                                 \
-        hipLaunchKernelGGL((gemv_kernel<T, TS, NVV, NB, GG, EPI>), grid, dim3(256), 0, s, a);   \
-        prof_end(a.prof, s);                                                                   \
-        break;
+template <typename T, int TS, int NV, int NB, int G, bool SIDE>
+int blocks_per_cu() {
+    static const int occ = [] {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &n, reinterpret_cast<const void*>(&gemv_kernel<T, TS, NV, NB, G, SIDE>),
+                BlockOf<SIDE>::value, 0) !=
+                hipSuccess ||
+            n < 1)
+            n = 1;
+        return n;
+    }();
+    return occ;
+}
+
+// Blocks per resident slot: 1 makes the grid exactly what the device holds at once.
+constexpr int kOversub = 1;
+
+// Shares the resident blocks among the segments in proportion to their groups of rows
+// (at least one each) and launches.
+template <typename T, int TS, int NV, int NB, int G, bool SIDE>
+hipError_t launch_shape(GemvArgs a, hipStream_t s) {
+    constexpr int NT = BlockOf<SIDE>::value / TS;
+    const int slots = blocks_per_cu<T, TS, NV, NB, G, SIDE>() * device_cus() * kOversub;
+    const int nside = SIDE ? a.nside : 0;
+    const int avail = slots - nside > 1 ? slots - nside : 1;
+    int want[kMaxSeg] = {0, 0, 0}, total_want = 0;
+    for (int i = 0; i < a.nseg; ++i) {
+        const long long rows_cap = (long long)a.seg[i].list.cap * a.seg[i].rpu;
+        const long long groups = (rows_cap + G - 1) / G;
+        want[i] = (int)((groups + NT - 1) / NT);
+        if (want[i] < 1) want[i] = 1;
+        total_want += want[i];
+    }
+    int total = 0;
+    for (int i = 0; i < a.nseg; ++i) {
+        int b = want[i];
+        if (total_want > avail) {
+            b = (int)((long long)avail * want[i] / total_want);
+            if (b < 1) b = 1;
+        }
+        a.seg[i].blocks = b;
+        total += b;
+    }
+    if (!SIDE) a.nside = 0;
+    dim3 grid(total + nside);
+    prof_begin(a.prof, s);
+    hipLaunchKernelGGL((gemv_kernel<T, TS, NV, NB, G, SIDE>), grid, dim3(BlockOf<SIDE>::value), 0, s, a);
+    prof_end(a.prof, s);
+    return hipGetLastError();
+}
+
+template <typename T, int TS, int NB, bool SIDE>
+hipError_t dispatch_nv(const GemvArgs& a, int nv, hipStream_t s) {
+#define DJV_GEMV_CASE(NVV, GG) \
+    case NVV:                  \
+        return launch_shape<T, TS, NVV, NB, GG, SIDE>(a, s);
     if constexpr (TS == 64) {
         switch (nv) {
             DJV_GEMV_CASE(1, 4)
-            DJV_GEMV_CASE(2, 4)
-            DJV_GEMV_CASE(3, 4)
+            DJV_GEMV_CASE(2, 2)
+            DJV_GEMV_CASE(3, 2)
         default:
             return hipErrorInvalidValue;
         }
     } else {
         switch (nv) {
-            DJV_GEMV_CASE(1, 4)
-            DJV_GEMV_CASE(2, 4)
-            DJV_GEMV_CASE(3, 3)
-            DJV_GEMV_CASE(4, 3)
-            DJV_GEMV_CASE(5, 2)
-            DJV_GEMV_CASE(6, 2)
-            DJV_GEMV_CASE(7, 2)
-            DJV_GEMV_CASE(8, 2)
+            DJV_GEMV_CASE(1, 2)
+            DJV_GEMV_CASE(2, 2)
+            DJV_GEMV_CASE(3, 1)
+            DJV_GEMV_CASE(4, 1)
+            DJV_GEMV_CASE(5, 1)
+            DJV_GEMV_CASE(6, 1)
+            DJV_GEMV_CASE(7, 1)
+            DJV_GEMV_CASE(8, 1)
         default:
             return hipErrorInvalidValue;
         }
     }
 #undef DJV_GEMV_CASE
-    return hipGetLastError();
 }
 
-// Chooses the team size, vectors per thread and rows per team, sizes each segment's
-// share of the grid, and launches.
-template <typename T, int EPI>
-hipError_t dispatch(const GemvArgs& a_in, hipStream_t s) {
+// Chooses the team size, vectors per thread and rows per team, and launches.
+template <typename T, bool SIDE>
+hipError_t dispatch(const GemvArgs& a, hipStream_t s) {
     constexpr int E = WTraits<T>::kPerVec;
-    GemvArgs a = a_in;
+    if (a.nseg < 1 || a.nseg > kMaxSeg || a.nside < 0 || a.nside > kMaxSide) return hipErrorInvalidValue;
     const int nvec = a.cols / E;
     const bool small = nvec <= 3 * 64;
     const int TS = small ? 64 : 256;
     const int nv = (nvec + TS - 1) / TS;
-    int G;
-    if (small) G = 4;
-    else G = nv <= 2 ? 4 : (nv <= 4 ? 3 : 2);
-    const int NT = 256 / TS;
-    const int max_blocks = 256 * 64;
-    int total = 0;
-    for (int i = 0; i < a.nseg; ++i) {
-        const int rows_cap = a.seg[i].list.cap * a.seg[i].rpu;
-        const int groups = (rows_cap + G - 1) / G;
-        int blocks = (groups + NT - 1) / NT;
-        if (blocks > max_blocks) blocks = max_blocks;
-        if (blocks < 1) blocks = 1;
-        a.seg[i].blocks = blocks;
-        total += blocks;
-    }
-    if (total <= 0) return hipSuccess;
-    dim3 grid(total);
     const int nb = a.B <= 1 ? 1 : (a.B <= 2 ? 2 : 4);
     if (small) {
-        if (nb == 1) return dispatch_nv<T, 64, 1, EPI>(a, nv, grid, s);
-        if (nb == 2) return dispatch_nv<T, 64, 2, EPI>(a, nv, grid, s);
-        return dispatch_nv<T, 64, 4, EPI>(a, nv, grid, s);
+        if (nb == 1) return dispatch_nv<T, 64, 1, SIDE>(a, nv, s);
+        if (nb == 2) return dispatch_nv<T, 64, 2, SIDE>(a, nv, s);
+        return dispatch_nv<T, 64, 4, SIDE>(a, nv, s);
     }
-    if (nb == 1) return dispatch_nv<T, 256, 1, EPI>(a, nv, grid, s);
-    if (nb == 2) return dispatch_nv<T, 256, 2, EPI>(a, nv, grid, s);
-    return dispatch_nv<T, 256, 4, EPI>(a, nv, grid, s);
+    if (nb == 1) return dispatch_nv<T, 256, 1, SIDE>(a, nv, s);
+    if (nb == 2) return dispatch_nv<T, 256, 2, SIDE>(a, nv, s);
+    return dispatch_nv<T, 256, 4, SIDE>(a, nv, s);
 }
 
 }  // namespace gemv_detail

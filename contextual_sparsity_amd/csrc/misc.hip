@@ -78,6 +78,19 @@ ProfHook& prof_hook() {
     return hook;
 }
 
+int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+            n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
 unsigned* device_flags() {
     static unsigned* addr[64] = {nullptr};
     int dev = 0;

@@ -88,7 +88,7 @@ def lib() -> ctypes.CDLL:
             "dejavu_sparse_layer": [ctypes.POINTER(djv_model), ctypes.POINTER(djv_layer), _P,
                                     ctypes.POINTER(djv_trace), _P, _SZ, _P],
             "dejavu_stack_decode": [ctypes.POINTER(djv_model), ctypes.POINTER(djv_layer), _I, _P, _I,
-                                    _I, ctypes.POINTER(djv_trace), _P, _SZ, _P, _P],
+                                    _I, ctypes.POINTER(djv_trace), _P, _SZ, _P],
             "dejavu_poll_device_error": [_P, ctypes.POINTER(ctypes.c_uint32)],
             "dejavu_profile_kernel": [_I, ctypes.POINTER(_P), _I],
             "dejavu_profile_count": [ctypes.POINTER(_I)],
@@ -249,14 +249,12 @@ def dejavu_sparse_layer(m: djv_model, layer: djv_layer, x, trace: Optional[djv_t
 
 
 def dejavu_stack_decode(m: djv_model, layers: Sequence[djv_layer], x, lookahead: bool, dense: bool,
-                        trace: Optional[djv_trace], ws, s_main=None, s_pred=None) -> None:
+                        trace: Optional[djv_trace], ws, stream=None) -> None:
     arr = (djv_layer * len(layers))(*layers)
     wp, wb = _ws(ws)
-    sm = _stream(s_main)
-    sp = _stream(s_pred) if s_pred is not None else sm
     _check(lib().dejavu_stack_decode(ctypes.byref(m), arr, len(layers), _ptr(x), int(lookahead),
                                      int(dense), ctypes.byref(trace) if trace is not None else None,
-                                     wp, wb, sm, sp))
+                                     wp, wb, _stream(stream)))
 
 
 def dejavu_poll_device_error(stream=None) -> int:

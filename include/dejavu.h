@@ -205,16 +205,18 @@ djv_status dejavu_sparse_layer(const djv_model* m, const djv_layer* layer, float
 /* --------------------------------------------------------------------------------------
  * dejavu_stack_decode -- one decode step through L layers (x [B, d] updated in place).
  *   lookahead = 1 ([BLOG section 3.1], [NOTES "Reducing Overhead with Asynchronous
- *   Execution"]): layer l+1's sets are predicted from y_l = LN(x_l) on `s_pred` while
- *   layer l computes on `s_main`; layer 0's sets are predicted first from LN(x_0).
- *   lookahead = 0: each layer as dejavu_sparse_layer, on s_main only.
- *   dense = 1: every layer dense (all heads and neurons, no predictor), on s_main only.
- *   layers: host array of L descriptors.  s_pred may equal s_main (no overlap).
- *   Two HIP events are created and released per call (no device memory is allocated).
+ *   Execution"]): layer l+1's sets are predicted from y_l = LN(x_l) while layer l
+ *   computes; layer 0's sets are predicted first from LN(x_0).  The overlap is inside
+ *   launches on the one stream: the predictor weights stream in the same launches as
+ *   layer l's weights and each selection runs in a side block of a later launch.
+ *   lookahead = 0: each layer as dejavu_sparse_layer.
+ *   dense = 1: every layer dense (all heads and neurons, no predictor).
+ *   layers: host array of L descriptors.  Everything is enqueued on `stream`; nothing is
+ *   allocated and nothing waits on the host.
  * ------------------------------------------------------------------------------------ */
 djv_status dejavu_stack_decode(const djv_model* m, const djv_layer* layers, int L, float* x,
                                int lookahead, int dense, const djv_trace* trace,
-                               void* ws, size_t ws_bytes, void* s_main, void* s_pred);
+                               void* ws, size_t ws_bytes, void* stream);
 
 /* dejavu_workspace_bytes_model -- workspace for dejavu_sparse_layer / dejavu_stack_decode. */
 djv_status dejavu_workspace_bytes_model(const djv_model* m, size_t* bytes);

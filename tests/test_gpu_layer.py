@@ -54,9 +54,8 @@ class Stack:
         if single_layer:
             dj.dejavu_sparse_layer(self.m, self.desc[0], x, tr, self.ws)
         else:
-            s_pred = torch.cuda.Stream()
             dj.dejavu_stack_decode(self.m, self.desc, x, lookahead, False, tr, self.ws,
-                                   torch.cuda.current_stream(), s_pred)
+                                   torch.cuda.current_stream())
         torch.cuda.synchronize()
         # no out-of-range index and no count above its list's capacity on the device
         assert dj.dejavu_poll_device_error() == 0

@@ -23,6 +23,36 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qkv_p1_launch_opt175b_traffic.txt")
+KERNEL_SOURCES = ["common.hpp", "gemv.hpp", "select.hpp", "attn.hpp", "gemv_f16_side.hip"]
+
+
+def kernel_sources_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "contextual_sparsity_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter summary
+    (rocprofv3 FETCH_SIZE and WRITE_SIZE, calibrated on a copy), or None when the kernel
+    sources changed since it was taken."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                if ":" in line and not line.startswith(("#", " ", "|")):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("sources_sha256") != kernel_sources_sha():
+            return None
+        return int(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def parse(argv=None):
@@ -39,6 +69,9 @@ def parse(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget")
     ap.add_argument("--breakdown", action="store_true", help="time every kernel family")
     ap.add_argument("--no-lookahead", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of 1 GiB three times (reference for HBM byte "
+                         "counters) and exit")
     return ap.parse_args(argv)
 
 
@@ -113,6 +146,18 @@ def main(argv=None) -> int:
     import torch
     from contextual_sparsity_amd import configs, synth
     from contextual_sparsity_amd import dejavu as dj
+
+    if args.calibrate_copy:
+        # a copy kernel of known size: its FETCH_SIZE / WRITE_SIZE per dispatch calibrate the
+        # byte counters (1 GiB read and 1 GiB written per copy)
+        src = torch.empty(2**30 // 4, dtype=torch.float32, device="cuda").normal_()
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": 2**30, "bytes_written": 2**30,
+                          "dispatches": 3}), flush=True)
+        return 0
 
     wl = configs.WORKLOADS[args.workload]
     s = wl.shape
@@ -214,6 +259,21 @@ def main(argv=None) -> int:
                  "bytes_per_layer": dense_layer_bytes(s)}
         log(f"dense step {ms_dense:.3f} ms")
 
+    # achievable HBM rate on this device: a plain device copy of 2 GiB (read + write bytes)
+    src = torch.empty(2**29, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ea.record()
+    for _ in range(5):
+        dst.copy_(src)
+    eb.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() * 4 * 5 / (ea.elapsed_time(eb) * 1e-3) / 1e9
+    del src, dst
+    log(f"device copy reference {copy_gbs:.0f} GB/s (read + write)")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("CPU oracle sample ...")
@@ -238,6 +298,8 @@ def main(argv=None) -> int:
                    "keep_heads_pct": wl.pct_A, "k_M": k_M, "k_A": k_A, "lookahead": lookahead},
         "us_per_layer": round(ms_step * 1e3 / L, 2),
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "copy_ref_GBps": round(copy_gbs, 1),
+        "pct_of_copy_ref": round(100 * gbs / copy_gbs, 2),
         "tokens_per_s": round(1e3 / ms_step, 1),
         "bytes_per_layer": lb,
         "wall_ms_per_step": round(wall_ms, 4),
@@ -246,7 +308,7 @@ def main(argv=None) -> int:
         "roofline": {"kernel": "Q/K/V of the kept heads + next layer's predictor first layers "
                                "(gemv_kernel, one launch per layer)", "bound": "hbm",
                      "achieved": round(qkv_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(qkv_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(qkv_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "bytes_per_launch": round(k1_bytes), "us_per_launch": round(qkv_ms * 1e3, 2),
                      "launches": qkv_n},
         "kernels": kernels or None,

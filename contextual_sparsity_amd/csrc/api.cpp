@@ -147,21 +147,24 @@ struct MlpWs { float* a; float* partial; int rpc; };
 MlpWs plan_mlp(Arena& A, int B, int d, int cap, bool f16) {
     MlpWs w;
     w.a = A.take<float>((size_t)B * (cap > 0 ? cap : 1));
-    const int nch = axpy_chunks(cap, d, f16, &w.rpc);
+    const int nch = axpy_chunks(cap, d, f16, 0, &w.rpc);
     w.partial = A.take<float>((size_t)nch * B * d);
     return w;
 }
 
-struct MhaWs { float* q; float* part; float* H; float* partial; int rpc, chunk, nchunk_max; };
+// fused: the O-projection merges the attention chunks itself (no merge kernel, no H);
+// possible when a head has at most kFuseMaxChunks chunks, with chunks of at most dh rows.
+struct MhaWs { float* q; float* part; float* H; float* partial; int rpc, chunk, nchunk_max; bool fused; };
 MhaWs plan_mha(Arena& A, int B, int d, int dh, int cap, int n_cap, bool f16) {
     MhaWs w;
     const int c = cap > 0 ? cap : 1;
     w.chunk = attn_chunk_for(f16, dh);
     w.nchunk_max = (n_cap + w.chunk - 1) / w.chunk;
+    w.fused = w.nchunk_max <= kFuseMaxChunks;
     w.q = A.take<float>((size_t)B * c * dh);
     w.part = A.take<float>((size_t)B * c * w.nchunk_max * (dh + 2));
     w.H = A.take<float>((size_t)B * c * dh);
-    const int nch = axpy_chunks(cap * dh, d, f16, &w.rpc);
+    const int nch = axpy_chunks(cap * dh, d, f16, w.fused ? dh : 0, &w.rpc);
     w.partial = A.take<float>((size_t)nch * B * d);
     return w;
 }
@@ -320,25 +323,37 @@ djv_status run_mlp(bool f16, int B, int d, int N, const RowInput& in, const void
     return run_down(f16, B, d, W2, list, resid, out, stats, w, s);
 }
 
-// Split-position attention over the kept heads and its merge (q from the QKV step).
-djv_status run_attend(bool f16, int B, int h, int dh, int n, int n_cap, void* Kc, void* Vc,
-                      const UnitList& heads, float scale, const MhaWs& w, hipStream_t s) {
+// Split-position attention over the kept heads (q from the QKV step).
+AttnArgs attend_args(int B, int h, int dh, int n, int n_cap, void* Kc, void* Vc,
+                     const UnitList& heads, float scale, const MhaWs& w) {
     AttnArgs at{};
     at.Kc = Kc; at.Vc = Vc; at.list = heads; at.h = h; at.dh = dh; at.n = n; at.n_cap = n_cap;
     at.B = B; at.q = w.q; at.scale = scale; at.part = w.part; at.chunk = w.chunk;
     at.nchunk = (n + 1 + w.chunk - 1) / w.chunk; at.H = w.H; at.flags = device_flags();
     at.prof = DJV_PROF_ATTN;
-    DJV_HIP(launch_attention(f16, at, s));
+    return at;
+}
+
+// The attention's own launches: the chunks, and the merge kernel unless the O-projection
+// merges them.
+djv_status run_attend(bool f16, int B, int h, int dh, int n, int n_cap, void* Kc, void* Vc,
+                      const UnitList& heads, float scale, const MhaWs& w, hipStream_t s) {
+    DJV_HIP(launch_attention(f16, attend_args(B, h, dh, n, n_cap, Kc, Vc, heads, scale, w), !w.fused, s));
     return DJV_OK;
 }
 
-// Row-axpy over the kept heads' W_O rows: out = resid + sum_i H_i W_i^O.
-djv_status run_oproj(bool f16, int B, int d, int dh, const void* Wo, const UnitList& heads,
+// Row-axpy over the kept heads' W_O rows: out = resid + sum_i H_i W_i^O (H merged from
+// the attention chunks here when fused).
+djv_status run_oproj(bool f16, int B, int d, int dh, int n, const void* Wo, const UnitList& heads,
                      const float* resid, float* out, float2* stats, const MhaWs& w, hipStream_t s) {
     AxpyArgs x{};
     x.W = Wo; x.cols = d; x.list = heads; x.rpu = dh; x.coef = w.H; x.ldc = heads.cap * dh; x.B = B;
     x.partial = w.partial; x.rows_per_chunk = w.rpc; x.resid = resid; x.out = out; x.stats = stats;
     x.flags = device_flags(); x.prof = DJV_PROF_O_PROJ;
+    if (w.fused) {
+        x.attn_part = w.part;
+        x.attn_nchunk = (n + 1 + w.chunk - 1) / w.chunk;
+    }
     DJV_HIP(launch_axpy(f16, x, s));
     return DJV_OK;
 }
@@ -355,7 +370,7 @@ djv_status run_mha(bool f16, int B, int d, int h, int dh, int n, int n_cap, cons
     add_seg(g, seg_qkv(Wqkv, heads, dh, in, w.q));
     DJV_HIP(launch_gemv(f16, g, s));
     DJV_TRY(run_attend(f16, B, h, dh, n, n_cap, Kc, Vc, heads, scale, w, s));
-    return run_oproj(f16, B, d, dh, Wo, heads, resid, out, stats, w, s);
+    return run_oproj(f16, B, d, dh, n, Wo, heads, resid, out, stats, w, s);
 }
 
 djv_status check_model(const djv_model* m) {
@@ -795,16 +810,25 @@ djv_status dejavu_stack_decode(const djv_model* m, const djv_layer* layers, int 
         DJV_HIP(launch_gemv(f16, g, sm));
         DJV_TRY(trace_sets(trace, *m, l, w, cur, sm));
 
-        DJV_TRY(run_attend(f16, m->B, m->h, m->dh, m->n, m->n_cap, Ly.Kc, Ly.Vc, heads, m->scale,
-                           w.mha, sm));
-        if (ahead) {
-            // P2 of both predictors for l+1
+        if (ahead && w.mha.fused) {
+            // P2 of both predictors for l+1, with the attention chunks in its first blocks
             g = gemv_args(m->r, m->B, DJV_PROF_PRED_2);
             add_seg(g, seg_second(na));
             add_seg(g, seg_second(nm));
+            g.attn = attend_args(m->B, m->h, m->dh, m->n, m->n_cap, Ly.Kc, Ly.Vc, heads, m->scale, w.mha);
+            g.nattn = m->B * capA * g.attn.nchunk;
             DJV_HIP(launch_gemv(f16, g, sm));
+        } else {
+            DJV_TRY(run_attend(f16, m->B, m->h, m->dh, m->n, m->n_cap, Ly.Kc, Ly.Vc, heads, m->scale,
+                               w.mha, sm));
+            if (ahead) {
+                g = gemv_args(m->r, m->B, DJV_PROF_PRED_2);
+                add_seg(g, seg_second(na));
+                add_seg(g, seg_second(nm));
+                DJV_HIP(launch_gemv(f16, g, sm));
+            }
         }
-        DJV_TRY(run_oproj(f16, m->B, m->d, m->dh, Ly.Wo, heads, io.x_in, w.xm, w.sm, w.mha, sm));
+        DJV_TRY(run_oproj(f16, m->B, m->d, m->dh, m->n, Ly.Wo, heads, io.x_in, w.xm, w.sm, w.mha, sm));
         if (trace && trace->x_mid)
             DJV_TRY(copy_async(trace->x_mid + (size_t)l * m->B * m->d, w.xm, (size_t)m->B * m->d * 4, sm));
 

@@ -14,8 +14,8 @@
 // its four waves stream their rows with kUnroll independent 16-byte loads in flight per
 // lane, combine in LDS and write one partial tile.
 // Kernel 2 (finalize): out = resid + the partial tiles summed in a fixed order, so the
-// result does not depend on scheduling (no atomics); a thread issues its loads in
-// batches before adding.  It also writes (mean, M2) of every 64-column slice of out, from
+// result does not depend on scheduling (no atomics); 16-byte loads, all of a thread's
+// chunks in flight together.  It also writes (mean, M2) of every 64-column slice of out, from
 // which the next GEMV applies LayerNorm while loading.  The kernel boundary between the
 // two is what makes the partial tiles of all XCDs visible; no device-wide fence is used.
 #include "common.hpp"
@@ -27,11 +27,80 @@ constexpr int kUnroll = 8;      // rows in flight per wave
 constexpr int kWavesPerBlock = 4;
 constexpr int kThreads = 256;
 
+// Coefficients of this chunk's rows merged from split-position attention partials: row
+// r = u * dh + c (unit slot u, dim c) of batch row b gets
+//   sum_ch e^{m_ch - M} acc_ch[c] / sum_ch e^{m_ch - M} l_ch,   M = max_ch m_ch,
+// the sums taken in chunk order ([NOTES "Sparsified Attention"]: H_i = D_i^{-1} exp(.) X
+// W_i^V, the chunks' maxima cancelling between numerator and D_i).  A chunk of at most dh
+// rows touches at most two unit slots; their (m, l) go through LDS first.
+template <int NB>
+__device__ __forceinline__ void stage_attention(const AxpyArgs& a, int r0, int nr, float* cf_s,
+                                                int* row_s, float* wm, float* wl, float* inv) {
+    const int tid = threadIdx.x, dh = a.rpu, nck = a.attn_nchunk, cap = a.list.cap;
+    const int u0 = r0 / dh;
+    const int nh = (r0 + nr - 1) / dh - u0 + 1;  // 1 or 2
+    const size_t stride = (size_t)dh + 2;
+    for (int i = tid; i < NB * 2 * nck; i += kThreads) {  // [b][h][ch]
+        const int ch = i % nck, h = (i / nck) % 2, b = i / (2 * nck);
+        float m = -INFINITY, l = 0.f;
+        if (b < a.B && h < nh) {
+            const float* pp = a.attn_part + (((size_t)b * cap + u0 + h) * nck + ch) * stride;
+            m = pp[0];
+            l = pp[1];
+        }
+        wm[i] = m;
+        wl[i] = l;
+    }
+    __syncthreads();
+    if (tid < NB * 2) {
+        // one thread per (b, h): chunk weights in place and the denominator, in chunk order
+        float* m = wm + tid * nck;
+        const float* l = wl + tid * nck;
+        float M = -INFINITY;
+        for (int ch = 0; ch < nck; ++ch) M = fmaxf(M, m[ch]);
+        float L = 0.f;
+        for (int ch = 0; ch < nck; ++ch) {
+            m[ch] = __expf(m[ch] - M);
+            L = fmaf(l[ch], m[ch], L);
+        }
+        inv[tid] = L;
+    }
+    __syncthreads();
+    for (int i = tid; i < nr; i += kThreads) {
+        const int r = r0 + i;
+        const int u = r / dh, c = r - u * dh, h = u - u0;
+        const int unit = unit_of(a.list, u, a.flags);
+        row_s[i] = unit < 0 ? -1 : unit * dh + c;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            float v = 0.f;
+            if (unit >= 0 && b < a.B) {
+                const float* pp = a.attn_part + ((size_t)b * cap + u) * nck * stride + 2 + c;
+                const float* w = wm + (b * 2 + h) * nck;
+                float acc = 0.f;
+                int ch = 0;
+                for (; ch + 8 <= nck; ch += 8) {
+                    float av[8];
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) av[k] = pp[(size_t)(ch + k) * stride];
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) acc = fmaf(av[k], w[ch + k], acc);
+                }
+                for (; ch < nck; ++ch) acc = fmaf(pp[(size_t)ch * stride], w[ch], acc);
+                v = acc / inv[b * 2 + h];
+            }
+            cf_s[b * a.rows_per_chunk + i] = v;
+        }
+    }
+}
+
 template <typename T, int NB>
 __global__ __launch_bounds__(kThreads) void axpy_partial_kernel(AxpyArgs a) {
     constexpr int E = WTraits<T>::kPerVec;
     constexpr int TC = kWave * E;                       // columns per tile
-    extern __shared__ float dyn[];                      // [NB][rpc] coefs, then [rpc] rows
+    // dynamic LDS: [NB][rpc] coefficients, [rpc] rows, then (merged attention) the
+    // [NB][2][nchunk] chunk maxima / weights and sums, and [NB][2] denominators
+    extern __shared__ float dyn[];
     __shared__ float red[kWavesPerBlock - 1][NB][TC];
 
     const int tid = threadIdx.x, wv = tid / kWave, ln = tid % kWave;
@@ -47,15 +116,21 @@ __global__ __launch_bounds__(kThreads) void axpy_partial_kernel(AxpyArgs a) {
     float* cf_s = dyn;
     int* row_s = reinterpret_cast<int*>(dyn + NB * a.rows_per_chunk);
 
-    // stage row numbers and coefficients of the chunk
-    for (int i = tid; i < nr; i += kThreads) {
-        const int r = r0 + i;
-        const int u = r / a.rpu, sub = r - u * a.rpu;
-        const int unit = unit_of(a.list, u, a.flags);
-        row_s[i] = unit < 0 ? -1 : unit * a.rpu + sub;
+    if (a.attn_part) {
+        float* wm = dyn + (NB + 1) * a.rows_per_chunk;
+        float* wl = wm + NB * 2 * a.attn_nchunk;
+        stage_attention<NB>(a, r0, nr, cf_s, row_s, wm, wl, wl + NB * 2 * a.attn_nchunk);
+    } else {
+        // stage row numbers and coefficients of the chunk
+        for (int i = tid; i < nr; i += kThreads) {
+            const int r = r0 + i;
+            const int u = r / a.rpu, sub = r - u * a.rpu;
+            const int unit = unit_of(a.list, u, a.flags);
+            row_s[i] = unit < 0 ? -1 : unit * a.rpu + sub;
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
-            cf_s[b * a.rows_per_chunk + i] = (unit >= 0 && b < a.B) ? a.coef[(size_t)b * a.ldc + r] : 0.f;
+            for (int b = 0; b < NB; ++b)
+                cf_s[b * a.rows_per_chunk + i] = (unit >= 0 && b < a.B) ? a.coef[(size_t)b * a.ldc + r] : 0.f;
+        }
     }
     __syncthreads();
 
@@ -121,45 +196,58 @@ __global__ __launch_bounds__(kThreads) void axpy_partial_kernel(AxpyArgs a) {
 }
 
 // out = resid + sum of the used partial tiles in a fixed order, per 64-column slice, and
-// the slice's (mean, M2).  Block (slice, b): four groups of 64 threads split the chunks
-// (group g adds chunks g, g+4, ...), then wave 0 adds the four group sums in order.
-constexpr int kFinGroups = 4;
-constexpr int kFinUnroll = 4;
+// the slice's (mean, M2).  Block (slice, b) of 256 threads: thread (g, q) loads float4 q
+// of the slice from chunks g, g+16, g+32, ... (all its loads in one round), the 16 group
+// sums are added in order through LDS, and one wave finishes the slice.
+constexpr int kFinGroups = 16;
+constexpr int kFinQuads = kLnTile / 4;   // float4 per 64-column slice
+constexpr int kFinBatch = 4;             // loads per thread in flight (chunks <= 64 in one round)
 
-__global__ __launch_bounds__(kWave * kFinGroups) void axpy_finalize_kernel(AxpyArgs a) {
-    __shared__ float red[kFinGroups - 1][kWave];
+__global__ __launch_bounds__(kFinGroups * kFinQuads) void axpy_finalize_kernel(AxpyArgs a) {
+    __shared__ float red[kFinGroups][kLnTile + 4];
     const int slice = blockIdx.x, b = blockIdx.y;
-    const int g = threadIdx.x / kWave, c = threadIdx.x % kWave;
-    const int col = slice * kWave + c;
-    const bool ok = col < a.cols;
+    const int g = threadIdx.x / kFinQuads, q = threadIdx.x % kFinQuads;
+    const int c0 = slice * kLnTile;
+    const int ncols = min(kLnTile, a.cols - c0);
     const int count = read_count(a.list, nullptr);
     const int rows = count * a.rpu;
     const int nch = (rows + a.rows_per_chunk - 1) / a.rows_per_chunk;
     const size_t plane = (size_t)a.B * a.cols;
-    const float* p = a.partial + (size_t)b * a.cols + (ok ? col : 0);
-    float s = 0.f;
-    for (int ch = g; ch < nch; ch += kFinGroups * kFinUnroll) {
-        float t[kFinUnroll];
+    // a whole float4 inside the row, or (ragged last slice) a clamped one whose sum is unused
+    const bool q_ok = 4 * q + 4 <= ncols;
+    const float* p = a.partial + (size_t)b * a.cols + c0 + (q_ok ? 4 * q : 0);
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int ch0 = g; ch0 < nch; ch0 += kFinGroups * kFinBatch) {
+        float4 t[kFinBatch];
 #pragma unroll
-        for (int k = 0; k < kFinUnroll; ++k) {
-            const int cc = ch + k * kFinGroups;
-            t[k] = (ok && cc < nch) ? p[(size_t)cc * plane] : 0.f;
+        for (int k = 0; k < kFinBatch; ++k) {
+            const int cc = min(ch0 + k * kFinGroups, nch - 1);
+            t[k] = *reinterpret_cast<const float4*>(p + (size_t)cc * plane);
         }
 #pragma unroll
-        for (int k = 0; k < kFinUnroll; ++k) s += t[k];
+        for (int k = 0; k < kFinBatch; ++k) {
+            if (ch0 + k * kFinGroups < nch) {
+                s.x += t[k].x; s.y += t[k].y; s.z += t[k].z; s.w += t[k].w;
+            }
+        }
     }
-    if (g > 0) red[g - 1][c] = s;
+    red[g][4 * q + 0] = s.x;
+    red[g][4 * q + 1] = s.y;
+    red[g][4 * q + 2] = s.z;
+    red[g][4 * q + 3] = s.w;
     __syncthreads();
-    if (g != 0) return;
+    if (threadIdx.x >= kWave) return;
+    const int c = threadIdx.x;
+    const bool ok = c < ncols;
+    float v = 0.f;
 #pragma unroll
-    for (int q = 0; q < kFinGroups - 1; ++q) s += red[q][c];
-    const size_t o = (size_t)b * a.cols + col;
-    if (ok && a.resid) s += a.resid[o];
-    if (ok) a.out[o] = s;
+    for (int k = 0; k < kFinGroups; ++k) v += red[k][c];
+    const size_t o = (size_t)b * a.cols + c0 + c;
+    if (ok && a.resid) v += a.resid[o];
+    if (ok) a.out[o] = v;
     if (a.stats) {
-        const int n = min(kWave, a.cols - slice * kWave);
-        const float mean = wave_sum(ok ? s : 0.f) / (float)n;
-        const float dv = ok ? s - mean : 0.f;
+        const float mean = wave_sum(ok ? v : 0.f) / (float)ncols;
+        const float dv = ok ? v - mean : 0.f;
         const float M2 = wave_sum(dv * dv);
         if (c == 0) a.stats[(size_t)b * gridDim.x + slice] = make_float2(mean, M2);
     }
@@ -173,7 +261,12 @@ hipError_t dispatch(const AxpyArgs& a, hipStream_t s) {
     const int nch = rows_cap > 0 ? (rows_cap + a.rows_per_chunk - 1) / a.rows_per_chunk : 0;
     if (nch > 0) {
         const int nb = a.B <= 1 ? 1 : (a.B <= 2 ? 2 : 4);
-        const size_t dyn = (size_t)a.rows_per_chunk * (nb * sizeof(float) + sizeof(int));
+        size_t dyn = (size_t)a.rows_per_chunk * (nb * sizeof(float) + sizeof(int));
+        if (a.attn_part) {
+            if (a.attn_nchunk < 1 || a.attn_nchunk > kFuseMaxChunks || a.rows_per_chunk > a.rpu)
+                return hipErrorInvalidValue;
+            dyn += ((size_t)nb * 2 * a.attn_nchunk * 2 + (size_t)nb * 2) * sizeof(float);
+        }
         dim3 grid(tiles, nch);
         prof_begin(a.prof, s);
         if (nb == 1) hipLaunchKernelGGL((axpy_partial_kernel<T, 1>), grid, dim3(kThreads), dyn, s, a);
@@ -183,14 +276,14 @@ hipError_t dispatch(const AxpyArgs& a, hipStream_t s) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    dim3 fgrid((a.cols + kWave - 1) / kWave, a.B);
-    hipLaunchKernelGGL(axpy_finalize_kernel, fgrid, dim3(kWave * kFinGroups), 0, s, a);
+    dim3 fgrid((a.cols + kLnTile - 1) / kLnTile, a.B);
+    hipLaunchKernelGGL(axpy_finalize_kernel, fgrid, dim3(kFinGroups * kFinQuads), 0, s, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-int axpy_chunks(int rows_cap, int cols, bool f16, int* rows_per_chunk) {
+int axpy_chunks(int rows_cap, int cols, bool f16, int max_rows_per_chunk, int* rows_per_chunk) {
     const int E = f16 ? 8 : 4;
     const int tiles = (cols / E + kWave - 1) / kWave;
     const int step = kWavesPerBlock * kUnroll;  // 32 rows: one pass of the block
@@ -207,6 +300,7 @@ int axpy_chunks(int rows_cap, int cols, bool f16, int* rows_per_chunk) {
     int rpc = (rows_cap + chunks - 1) / chunks;
     rpc = ((rpc + step - 1) / step) * step;
     if (rpc > kAxpyMaxChunkRows) rpc = kAxpyMaxChunkRows;
+    if (max_rows_per_chunk > 0 && rpc > max_rows_per_chunk) rpc = max_rows_per_chunk;
     *rows_per_chunk = rpc;
     return (rows_cap + rpc - 1) / rpc;
 }

@@ -224,6 +224,24 @@ struct RowInput {
     float eps;
 };
 
+constexpr int kAttnMaxChunks = 1024;   // chunks per head the merge kernel accepts
+constexpr int kFuseMaxChunks = 128;    // chunks per head the O-projection merges itself
+
+struct AttnArgs {
+    const void* Kc;       // [B, h, n_cap, dh]
+    const void* Vc;
+    UnitList list;        // heads
+    int h, dh, n, n_cap, B;
+    const float* q;       // [B, cap, dh]
+    float scale;
+    float* part;          // [B, cap, nchunk, dh + 2]
+    int chunk;            // positions per chunk
+    int nchunk;
+    float* H;             // [B, cap, dh] (when merged by the merge kernel)
+    unsigned* flags;
+    int prof;
+};
+
 struct SelectJob {
     const float* z;       // [B, n_out]
     int n_out;
@@ -251,6 +269,7 @@ struct GemvSeg {
 
 constexpr int kMaxSeg = 3;
 constexpr int kMaxSide = 2;
+constexpr int kShortRows = 256;  // selections of rows up to this long fit any block size
 
 struct GemvArgs {
     GemvSeg seg[kMaxSeg];
@@ -265,6 +284,10 @@ struct GemvArgs {
     // scores (union in the block), independent of the GEMV segments
     SelectJob side[kMaxSide];
     int nside;
+    // attention chunks run by the first nattn blocks (256-thread launches), before the side
+    // selections and the GEMV segments; independent of both
+    AttnArgs attn;
+    int nattn;
     unsigned* flags;
     int prof;             // profiling family of this launch (0: none)
 };
@@ -284,32 +307,23 @@ struct AxpyArgs {
     const float* resid;   // may be nullptr
     float* out;           // [B, cols]
     float2* stats;        // [B, ceil(cols / kLnTile)] (mean, M2) of each slice of out, or nullptr
+    // when set, the coefficients are the attention outputs merged here from the
+    // split-position partials [B, cap, nchunk, rpu + 2] (rows of a unit = its rpu dims;
+    // needs rows_per_chunk <= rpu and nchunk <= kFuseMaxChunks); coef is then unused
+    const float* attn_part;
+    int attn_nchunk;
     unsigned* flags;
     int prof;
 };
 
 hipError_t launch_axpy(bool f16, const AxpyArgs& a, hipStream_t s);
-int axpy_chunks(int rows_cap, int cols, bool f16, int* rows_per_chunk);
+// Chunks of rows for a row-axpy over rows_cap rows (max_rows_per_chunk: 0 = no limit).
+int axpy_chunks(int rows_cap, int cols, bool f16, int max_rows_per_chunk, int* rows_per_chunk);
 constexpr int kAxpyMaxChunkRows = 1024;
 
-struct AttnArgs {
-    const void* Kc;       // [B, h, n_cap, dh]
-    const void* Vc;
-    UnitList list;        // heads
-    int h, dh, n, n_cap, B;
-    const float* q;       // [B, cap, dh]
-    float scale;
-    float* part;          // [B, cap, nchunk, dh + 2]
-    int chunk;            // positions per chunk
-    int nchunk;
-    float* H;             // [B, cap, dh]
-    unsigned* flags;
-    int prof;
-};
-
-hipError_t launch_attention(bool f16, const AttnArgs& a, hipStream_t s);
+// Partial (split-position) attention; with merge, also the merge kernel that writes H.
+hipError_t launch_attention(bool f16, const AttnArgs& a, bool merge, hipStream_t s);
 int attn_chunk_for(bool f16, int dh);  // positions per attention chunk
-constexpr int kAttnMaxChunks = 1024;   // chunks per head the merge kernel accepts
 
 hipError_t launch_select(const SelectJob* jobs, int njobs, int B, hipStream_t s, int prof);
 

@@ -1,5 +1,5 @@
-// Dispatch of the row-gather GEMV to its instantiations (weight dtype x with or without
-// side selections, each compiled in its own translation unit).
+// Dispatch of the row-gather GEMV to its instantiations (weight dtype x block size, each
+// compiled in its own translation unit).
 #include "common.hpp"
 
 namespace djv {
@@ -10,11 +10,23 @@ hipError_t launch_gemv_f16(const GemvArgs& a, hipStream_t s);
 hipError_t launch_gemv_f16_side(const GemvArgs& a, hipStream_t s);
 
 hipError_t launch_gemv(bool f16, const GemvArgs& a, hipStream_t s) {
-    if (a.nseg < 1 || a.nseg > kMaxSeg || a.nside < 0 || a.nside > kMaxSide) return hipErrorInvalidValue;
+    if (a.nseg < 1 || a.nseg > kMaxSeg || a.nside < 0 || a.nside > kMaxSide || a.nattn < 0)
+        return hipErrorInvalidValue;
     for (int i = 0; i < a.nseg; ++i)
         if (a.seg[i].epi < kEpiStore || a.seg[i].epi > kEpiQkv) return hipErrorInvalidValue;
-    if (f16) return a.nside > 0 ? launch_gemv_f16_side(a, s) : launch_gemv_f16(a, s);
-    return a.nside > 0 ? launch_gemv_f32_side(a, s) : launch_gemv_f32(a, s);
+    bool long_rows = false;
+    for (int i = 0; i < a.nside; ++i) long_rows = long_rows || a.side[i].n_out > kShortRows;
+    if (long_rows && (a.nattn > 0 || a.B > 1)) {
+        // no side-block form for this launch: the selections run first, on their own (their
+        // inputs are ready before the launch, so the results are the same)
+        hipError_t e = launch_select(a.side, a.nside, a.B, s, 0);
+        if (e != hipSuccess) return e;
+        GemvArgs b = a;
+        b.nside = 0;
+        return f16 ? launch_gemv_f16(b, s) : launch_gemv_f32(b, s);
+    }
+    if (f16) return long_rows ? launch_gemv_f16_side(a, s) : launch_gemv_f16(a, s);
+    return long_rows ? launch_gemv_f32_side(a, s) : launch_gemv_f32(a, s);
 }
 
 }  // namespace djv

@@ -32,6 +32,7 @@
 //     running alone on one compute unit.
 #pragma once
 #include "common.hpp"
+#include "attn.hpp"
 #include "select.hpp"
 
 namespace djv {
@@ -154,12 +155,11 @@ __device__ __forceinline__ float load_bias<__half>(const void* bias, int unit) {
     return (unit & 1) ? hi_h(w) : lo_h(w);
 }
 
-// Block sizes: launches that carry side selections use 1024-thread blocks (a selection
-// block needs them); the others use 256-thread blocks, which the hardware schedules with
-// less coupling between teams.
-constexpr int kSideThreads = 1024;
-constexpr int kPlainThreads = 256;
-template <bool SIDE> struct BlockOf { static constexpr int value = SIDE ? kSideThreads : kPlainThreads; };
+// Launch modes.  0: GEMV only.  1: the first blocks run attention chunks and selections
+// of short rows (at most 256 scores), then the GEMV.  2: the first blocks run selections of
+// long rows, which need 1024-thread blocks, then the GEMV.  Modes 0 and 1 use 256-thread
+// blocks, which the hardware schedules with less coupling between teams.
+template <int MODE> struct BlockOf { static constexpr int value = MODE == 2 ? 1024 : 256; };
 
 // A row of zeros as long as the longest supported row: a group slot with no row (past
 // the end of the list, or a skipped unit) loads from here, so every load is issued
@@ -174,15 +174,29 @@ struct Group {
     float bias[G];
 };
 
-template <typename T, int TS, int NV, int NB, int G, bool SIDE>
-__global__ __launch_bounds__(BlockOf<SIDE>::value) void gemv_kernel(GemvArgs a) {
-    constexpr int kThreads = BlockOf<SIDE>::value;
-    if constexpr (SIDE) {
-        if ((int)blockIdx.x < a.nside) {
+template <typename T, int TS, int NV, int NB, int G, int MODE>
+__global__ __launch_bounds__(BlockOf<MODE>::value) void gemv_kernel(GemvArgs a) {
+    constexpr int kThreads = BlockOf<MODE>::value;
+    int bid = (int)blockIdx.x;
+    if constexpr (MODE == 2) {
+        if (bid < a.nside) {
             __shared__ sel::RowShared SS;
-            sel::select_union_block(SS, a.side[blockIdx.x], a.B);
+            sel::select_one_row_block(SS, a.side[bid]);  // mode 2 runs with one batch row
             return;
         }
+        bid -= a.nside;
+    }
+    if constexpr (MODE == 1) {
+        if (bid < a.nattn) {
+            attn::attn_block<T>(a.attn, bid);
+            return;
+        }
+        if (bid < a.nattn + a.nside) {
+            __shared__ sel::SmallShared<kShortRows> SS;
+            sel::select_small_block<kShortRows>(SS, a.side[bid - a.nattn], a.B);
+            return;
+        }
+        bid -= a.nattn + a.nside;
     }
     constexpr int E = WTraits<T>::kPerVec;
     constexpr int NT = kThreads / TS;
@@ -194,7 +208,6 @@ __global__ __launch_bounds__(BlockOf<SIDE>::value) void gemv_kernel(GemvArgs a) 
     // is uniform over the wave and lives in scalar registers
     const int tm = __builtin_amdgcn_readfirstlane(tid / TS);
     const int lt = tid % TS, wv = lt / kWave, ln = tid % kWave;
-    int bid = (int)blockIdx.x - (SIDE ? a.nside : 0);
     int sg = 0;
 #pragma unroll
     for (int i = 0; i + 1 < kMaxSeg; ++i)
@@ -357,13 +370,13 @@ __global__ __launch_bounds__(BlockOf<SIDE>::value) void gemv_kernel(GemvArgs a) 
     }
 }
 
-template <typename T, int TS, int NV, int NB, int G, bool SIDE>
+template <typename T, int TS, int NV, int NB, int G, int MODE>
 int blocks_per_cu() {
     static const int occ = [] {
         int n = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &n, reinterpret_cast<const void*>(&gemv_kernel<T, TS, NV, NB, G, SIDE>),
-                BlockOf<SIDE>::value, 0) !=
+                &n, reinterpret_cast<const void*>(&gemv_kernel<T, TS, NV, NB, G, MODE>),
+                BlockOf<MODE>::value, 0) !=
                 hipSuccess ||
             n < 1)
             n = 1;
@@ -377,12 +390,14 @@ constexpr int kOversub = 1;
 
 // Shares the resident blocks among the segments in proportion to their groups of rows
 // (at least one each) and launches.
-template <typename T, int TS, int NV, int NB, int G, bool SIDE>
+template <typename T, int TS, int NV, int NB, int G, int MODE>
 hipError_t launch_shape(GemvArgs a, hipStream_t s) {
-    constexpr int NT = BlockOf<SIDE>::value / TS;
-    const int slots = blocks_per_cu<T, TS, NV, NB, G, SIDE>() * device_cus() * kOversub;
-    const int nside = SIDE ? a.nside : 0;
-    const int avail = slots - nside > 1 ? slots - nside : 1;
+    constexpr int NT = BlockOf<MODE>::value / TS;
+    const int slots = blocks_per_cu<T, TS, NV, NB, G, MODE>() * device_cus() * kOversub;
+    if (MODE != 1) a.nattn = 0;
+    if (MODE == 0) a.nside = 0;
+    const int nprefix = a.nattn + a.nside;
+    const int avail = slots - nprefix > 1 ? slots - nprefix : 1;
     int want[kMaxSeg] = {0, 0, 0}, total_want = 0;
     for (int i = 0; i < a.nseg; ++i) {
         const long long rows_cap = (long long)a.seg[i].list.cap * a.seg[i].rpu;
@@ -401,19 +416,18 @@ hipError_t launch_shape(GemvArgs a, hipStream_t s) {
         a.seg[i].blocks = b;
         total += b;
     }
-    if (!SIDE) a.nside = 0;
-    dim3 grid(total + nside);
+    dim3 grid(total + nprefix);
     prof_begin(a.prof, s);
-    hipLaunchKernelGGL((gemv_kernel<T, TS, NV, NB, G, SIDE>), grid, dim3(BlockOf<SIDE>::value), 0, s, a);
+    hipLaunchKernelGGL((gemv_kernel<T, TS, NV, NB, G, MODE>), grid, dim3(BlockOf<MODE>::value), 0, s, a);
     prof_end(a.prof, s);
     return hipGetLastError();
 }
 
-template <typename T, int TS, int NB, bool SIDE>
+template <typename T, int TS, int NB, int MODE>
 hipError_t dispatch_nv(const GemvArgs& a, int nv, hipStream_t s) {
 #define DJV_GEMV_CASE(NVV, GG) \
     case NVV:                  \
-        return launch_shape<T, TS, NVV, NB, GG, SIDE>(a, s);
+        return launch_shape<T, TS, NVV, NB, GG, MODE>(a, s);
     if constexpr (TS == 64) {
         switch (nv) {
             DJV_GEMV_CASE(1, 4)
@@ -440,7 +454,7 @@ hipError_t dispatch_nv(const GemvArgs& a, int nv, hipStream_t s) {
 }
 
 // Chooses the team size, vectors per thread and rows per team, and launches.
-template <typename T, bool SIDE>
+template <typename T, int MODE>
 hipError_t dispatch(const GemvArgs& a, hipStream_t s) {
     constexpr int E = WTraits<T>::kPerVec;
     if (a.nseg < 1 || a.nseg > kMaxSeg || a.nside < 0 || a.nside > kMaxSide) return hipErrorInvalidValue;
@@ -449,14 +463,21 @@ hipError_t dispatch(const GemvArgs& a, hipStream_t s) {
     const int TS = small ? 64 : 256;
     const int nv = (nvec + TS - 1) / TS;
     const int nb = a.B <= 1 ? 1 : (a.B <= 2 ? 2 : 4);
-    if (small) {
-        if (nb == 1) return dispatch_nv<T, 64, 1, SIDE>(a, nv, s);
-        if (nb == 2) return dispatch_nv<T, 64, 2, SIDE>(a, nv, s);
-        return dispatch_nv<T, 64, 4, SIDE>(a, nv, s);
+    if constexpr (MODE == 2) {
+        // long-row side selections are compiled for one batch row only (the launcher runs
+        // them separately otherwise)
+        if (nb != 1) return hipErrorInvalidValue;
+        return small ? dispatch_nv<T, 64, 1, MODE>(a, nv, s) : dispatch_nv<T, 256, 1, MODE>(a, nv, s);
+    } else {
+        if (small) {
+            if (nb == 1) return dispatch_nv<T, 64, 1, MODE>(a, nv, s);
+            if (nb == 2) return dispatch_nv<T, 64, 2, MODE>(a, nv, s);
+            return dispatch_nv<T, 64, 4, MODE>(a, nv, s);
+        }
+        if (nb == 1) return dispatch_nv<T, 256, 1, MODE>(a, nv, s);
+        if (nb == 2) return dispatch_nv<T, 256, 2, MODE>(a, nv, s);
+        return dispatch_nv<T, 256, 4, MODE>(a, nv, s);
     }
-    if (nb == 1) return dispatch_nv<T, 256, 1, SIDE>(a, nv, s);
-    if (nb == 2) return dispatch_nv<T, 256, 2, SIDE>(a, nv, s);
-    return dispatch_nv<T, 256, 4, SIDE>(a, nv, s);
 }
 
 }  // namespace gemv_detail

@@ -18,6 +18,12 @@ __global__ __launch_bounds__(kThreads) void select_rows_kernel(SelectJobs jobs, 
     finish_row(S, J, blockIdx.x, B, (J.n_out + 31) / 32);
 }
 
+// Rows of at most 1024 scores: one block per selection over all B rows.
+__global__ __launch_bounds__(kThreads) void select_small_kernel(SelectJobs jobs, int B) {
+    __shared__ SmallShared<kThreads> S;
+    select_small_block<kThreads>(S, jobs.j[blockIdx.x], B);
+}
+
 __global__ __launch_bounds__(kThreads) void compact_kernel(SelectJobs jobs, int B) {
     const SelectJob& J = jobs.j[blockIdx.x];
     const int tid = threadIdx.x;
@@ -39,7 +45,17 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(SelectJobs jobs, int 
 hipError_t launch_select(const SelectJob* jobs, int njobs, int B, hipStream_t s, int prof) {
     if (njobs < 1 || njobs > 2 || B < 1) return hipErrorInvalidValue;
     SelectJobs js{};
-    for (int i = 0; i < njobs; ++i) js.j[i] = jobs[i];
+    bool small = true;
+    for (int i = 0; i < njobs; ++i) {
+        js.j[i] = jobs[i];
+        small = small && jobs[i].n_out <= kThreads;
+    }
+    if (small) {
+        prof_begin(prof, s);
+        hipLaunchKernelGGL(select_small_kernel, dim3(njobs), dim3(kThreads), 0, s, js, B);
+        prof_end(prof, s);
+        return hipGetLastError();
+    }
     prof_begin(prof, s);
     hipLaunchKernelGGL(select_rows_kernel, dim3(B, njobs), dim3(kThreads), 0, s, js, B);
     prof_end(prof, s);

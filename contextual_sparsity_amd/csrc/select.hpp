@@ -9,7 +9,7 @@
 // bits.  A batch computes with the union of its rows' sets, listed in ascending order.
 //
 // Scores become order-preserving uint32 keys.  One 1024-thread block per row holds all
-// of the row's keys in registers (one round of loads; n <= 65536).  For top-k the k-th
+// of the row's keys in registers (one round of loads; n <= 49152).  For top-k the k-th
 // largest key is bracketed from a sample: 2048 scores spread evenly over the row are
 // histogrammed on their top 12 bits, and the bins holding the sample ranks k*2048/n -+ 4
 // standard deviations give a digit range [b_lo, b_hi].  Exact counts over all keys then
@@ -19,8 +19,8 @@
 // offsets from a block prefix count, and a radix select over their digits (12, 10, 10
 // bits) finds the k-th key; keys equal to it are taken in index order.  The bracket only
 // decides how much work is done, never the result: when the check fails (a sample far
-// off, or heavy ties) the row falls back to a radix select over all keys, reloading them
-// per pass.  Threshold rows are ballots of key > tau.  With one row the block compacts
+// off, or heavy ties), and for rows above 49152, the row falls back to a radix select
+// over all keys, reloading them per pass.  Threshold rows are ballots of key > tau.  With one row the block compacts
 // the result into the ascending index list and the device-side count; several rows are
 // ORed (in LDS for a side block, or by a second kernel).
 //
@@ -33,7 +33,7 @@ namespace djv {
 namespace sel {
 
 constexpr int kThreads = 1024;
-constexpr int kChunk = 32;                         // keys per thread held in registers at once
+constexpr int kChunk = 8;                          // keys per thread per round (radix path)
 constexpr int kMaxWords = kThreads * 2;            // 65536 bits
 constexpr int kMaxBins = 4096;                     // first digit: the top 12 bits of a key
 constexpr int kMaxCand = 4096;                     // candidates refined in LDS
@@ -241,6 +241,7 @@ __device__ __forceinline__ void select_row_radix(RowShared& S, const SelectJob& 
     __syncthreads();
 
     if (J.mode == 1) {
+#pragma unroll 1
         for (int rr = 0; rr < rounds; ++rr) {
             uint32_t kk[kChunk];
             load_keys(kk, rr);
@@ -258,6 +259,7 @@ __device__ __forceinline__ void select_row_radix(RowShared& S, const SelectJob& 
         // of 64 spare bins, one per lane, so they neither count nor collide)
         for (int i = tid; i < kMaxBins + kWave; i += kThreads) S.hist[i] = 0u;
         __syncthreads();
+#pragma unroll 1
         for (int rr = 0; rr < rounds; ++rr) {
             uint32_t kk[kChunk];
             load_keys(kk, rr);
@@ -280,7 +282,8 @@ __device__ __forceinline__ void select_row_radix(RowShared& S, const SelectJob& 
             // and index; one LDS atomic per wave and slot) and finished alone
             if (tid == 0) S.sh[2] = 0;
             __syncthreads();
-            for (int rr = 0; rr < rounds; ++rr) {
+    #pragma unroll 1
+        for (int rr = 0; rr < rounds; ++rr) {
                 uint32_t kk[kChunk];
                 load_keys(kk, rr);
 #pragma unroll
@@ -313,7 +316,8 @@ __device__ __forceinline__ void select_row_radix(RowShared& S, const SelectJob& 
                 const int shift = pass == 1 ? 10 : 0;
                 for (int i = tid; i < 1024; i += kThreads) S.hist[i] = 0u;
                 __syncthreads();
-                for (int rr = 0; rr < rounds; ++rr) {
+        #pragma unroll 1
+        for (int rr = 0; rr < rounds; ++rr) {
                     uint32_t kk[kChunk];
                     load_keys(kk, rr);
 #pragma unroll
@@ -328,7 +332,8 @@ __device__ __forceinline__ void select_row_radix(RowShared& S, const SelectJob& 
                 prefix |= (uint32_t)find_bin<kThreads, 4>(S.hist, 1024, rem, S.wtot, S.sh) << shift;
                 pmask |= 1023u << shift;
             }
-            for (int rr = 0; rr < rounds; ++rr) {
+    #pragma unroll 1
+        for (int rr = 0; rr < rounds; ++rr) {
                 uint32_t kk[kChunk];
                 load_keys(kk, rr);
 #pragma unroll
@@ -508,18 +513,28 @@ __device__ __forceinline__ bool select_row_fast(RowShared& S, const SelectJob& J
     return true;
 }
 
-// The whole selection of row b in one block: keys in registers, with the radix path as
-// the fallback.
+// The whole selection of row b in one block: keys in registers (rows up to 49152), with
+// the radix path for longer rows and as the fallback.
 __device__ __forceinline__ void select_row_full(RowShared& S, const SelectJob& J, int b) {
     const int n = J.n_out;
-    bool done;
+    bool done = false;
     if (n <= 16 * kThreads) done = select_row_fast<16>(S, J, b);
     else if (n <= 48 * kThreads) done = select_row_fast<48>(S, J, b);
-    else done = select_row_fast<64>(S, J, b);
     if (!done) {
         __syncthreads();
         select_row_radix(S, J, b);
     }
+}
+
+// Selection of a single row in this block, compacted into J.idx / J.count.
+__device__ __forceinline__ void select_one_row_block(RowShared& S, const SelectJob& J) {
+    const int tid = threadIdx.x;
+    const int words = (J.n_out + 31) / 32;
+    select_row_full(S, J, 0);
+    __syncthreads();
+    const int w0 = 2 * tid, w1 = 2 * tid + 1;
+    const int total = compact_words(w0 < words ? S.selw[w0] : 0u, w1 < words ? S.selw[w1] : 0u, J.idx, S.wtot);
+    if (tid == 0) *J.count = total;
 }
 
 // Selection over all B rows of J in this block, the union compacted into J.idx / J.count
@@ -544,6 +559,52 @@ __device__ __forceinline__ void select_union_block(RowShared& S, const SelectJob
     }
     const int w0 = 2 * tid, w1 = 2 * tid + 1;
     const int total = compact_words(w0 < words ? src[w0] : 0u, w1 < words ? src[w1] : 0u, J.idx, S.wtot);
+    if (tid == 0) *J.count = total;
+}
+
+// ---------------------------------------------------------------------------------
+// Rows of at most NT scores (the head predictor): one key per thread, ranks by counting
+// (keys above, plus equal keys at smaller indices), the union over the B rows, and an
+// ascending compaction from wave ballots.  Any block size NT.
+// ---------------------------------------------------------------------------------
+template <int NT>
+struct SmallShared {
+    uint32_t keys[NT];
+    int wtot[NT / kWave];
+};
+
+template <int NT>
+__device__ __forceinline__ void select_small_block(SmallShared<NT>& S, const SelectJob& J, int B) {
+    const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+    const int n = J.n_out;
+    bool sel = false;
+    for (int b = 0; b < B; ++b) {
+        const uint32_t key = score_key(J.z[(size_t)b * n + min(tid, n - 1)]);
+        if (J.mode == 1) {
+            sel = sel || (tid < n && key > J.tau_key);
+        } else {
+            S.keys[tid] = tid < n ? key : 0u;
+            __syncthreads();
+            int rank = 0;
+            for (int j = 0; j < n; ++j) {
+                const uint32_t kj = S.keys[j];
+                rank += (kj > key || (kj == key && j < tid)) ? 1 : 0;
+            }
+            sel = sel || (tid < n && rank < J.k);
+            __syncthreads();
+        }
+    }
+    const unsigned long long m = __ballot(sel);
+    if (lane == 0) S.wtot[w] = __popcll(m);
+    __syncthreads();
+    int base = 0, total = 0;
+#pragma unroll
+    for (int q = 0; q < NT / kWave; ++q) {
+        const int t = S.wtot[q];
+        if (q < w) base += t;
+        total += t;
+    }
+    if (sel) J.idx[base + __popcll(m & ((1ull << lane) - 1ull))] = tid;
     if (tid == 0) *J.count = total;
 }
 

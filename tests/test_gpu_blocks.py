@@ -18,6 +18,10 @@ SHAPES = {
     "f16-ragged": synth.LayerShape(d=1032, N=1500, h=6, dh=128, n=300, r=136, dtype="f16"),
     "opt125m": synth.LayerShape(d=768, N=3072, h=12, dh=64, n=128, r=128, dtype="f32"),
     "f16-wide": synth.LayerShape(d=4096, N=4000, h=8, dh=128, n=1024, r=1024, dtype="f16"),
+    # rows of 128+ 64-column slices: the one-kernel column-slice row-axpy, with a ragged
+    # last slice, and (N rows) more rows than one staging batch
+    "f32-slice": synth.LayerShape(d=8184, N=5000, h=4, dh=64, n=200, r=256, dtype="f32"),
+    "f16-slice": synth.LayerShape(d=8200, N=6000, h=4, dh=128, n=100, r=512, dtype="f16"),
 }
 
 

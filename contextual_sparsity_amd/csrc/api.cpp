@@ -6,7 +6,9 @@
 // dejavu_poll_device_error).
 #include "dejavu.h"
 
+#include <algorithm>
 #include <cmath>
+#include <initializer_list>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -63,6 +65,16 @@ djv_status check_dtype(int wt) {
 djv_status check_batch(int B) {
     DJV_REQUIRE(B >= 1, DJV_EINVAL, "B must be >= 1 (got %d)", B);
     DJV_REQUIRE(B <= DJV_MAX_BATCH, DJV_EUNSUPPORTED, "B = %d exceeds this build's limit %d", B, DJV_MAX_BATCH);
+    return DJV_OK;
+}
+// Batches above kMaxBatch run on the matrix cores: fp16 weights, and every GEMV row length
+// a multiple of the instruction's k (32).
+djv_status check_wide_batch(int B, int wt, std::initializer_list<int> cols) {
+    if (B <= kMaxBatch) return DJV_OK;
+    DJV_REQUIRE(wt == DJV_F16, DJV_EUNSUPPORTED, "B = %d > %d needs fp16 weights", B, kMaxBatch);
+    for (int c : cols)
+        DJV_REQUIRE(c % 32 == 0, DJV_EUNSUPPORTED, "B = %d > %d needs row lengths that are multiples of 32 (got %d)",
+                    B, kMaxBatch, c);
     return DJV_OK;
 }
 djv_status check_rowlen(int cols, int wt, const char* name) {
@@ -134,38 +146,59 @@ struct Arena {
     }
 };
 
-struct PredWs { float* u; float* z; uint32_t* bits; };
-PredWs plan_predict(Arena& A, int B, int r, int n_out, bool need_z) {
+// Scratch of the matrix-core GEMV (batches above kMaxBatch): the fp16 activation copies and
+// the k-slice partials.  A launch over R weight rows in T 16-row tiles takes S slices, S
+// doubling while T * S < 2048, so S == 1 or T * S < 4096; its S * R * bpad partial floats
+// are then at most max(R, 4096 * 16) * bpad.  Plans size the partials by that bound on the
+// largest R of their launches, which holds whichever launch a schedule makes.
+struct MfmaWs { __half* yh; float* part; };
+long long mfma_floats(int B, long long max_rows) {
+    const long long bpad = B <= 16 ? 16 : 32;
+    return std::max(max_rows, 4096LL * 16) * bpad;
+}
+MfmaWs plan_mfma(Arena& A, int B, int max_cols, long long floats) {
+    if (B <= kMaxBatch) return MfmaWs{nullptr, nullptr};
+    MfmaWs w;
+    w.yh = A.take<__half>((size_t)kMaxSeg * kMaxBatchMfma * max_cols);
+    w.part = A.take<float>((size_t)floats);
+    return w;
+}
+
+struct PredWs { float* u; float* z; uint32_t* bits; MfmaWs mf; };
+PredWs plan_predict(Arena& A, int B, int d, int r, int n_out, bool need_z) {
     PredWs w;
     w.u = A.take<float>((size_t)B * r);
     w.z = need_z ? A.take<float>((size_t)B * n_out) : nullptr;
     w.bits = A.take<uint32_t>((size_t)B * words_of(n_out));
+    w.mf = plan_mfma(A, B, std::max(d, r), mfma_floats(B, std::max(r, n_out)));
     return w;
 }
 
-struct MlpWs { float* a; float* partial; int rpc; };
+struct MlpWs { float* a; float* partial; int rpc; MfmaWs mf; };
 MlpWs plan_mlp(Arena& A, int B, int d, int cap, bool f16) {
     MlpWs w;
     w.a = A.take<float>((size_t)B * (cap > 0 ? cap : 1));
     const int nch = axpy_chunks(cap, d, f16, 0, &w.rpc);
     w.partial = A.take<float>((size_t)nch * B * d);
+    w.mf = plan_mfma(A, B, d, mfma_floats(B, cap));
     return w;
 }
 
 // fused: the O-projection merges the attention chunks itself (no merge kernel, no H);
 // possible when a head has at most kFuseMaxChunks chunks, with chunks of at most dh rows.
-struct MhaWs { float* q; float* part; float* H; float* partial; int rpc, chunk, nchunk_max; bool fused; };
+struct MhaWs { float* q; float* part; float* H; float* partial; int rpc, chunk, nchunk_max; bool fused; MfmaWs mf; };
 MhaWs plan_mha(Arena& A, int B, int d, int dh, int cap, int n_cap, bool f16) {
     MhaWs w;
     const int c = cap > 0 ? cap : 1;
     w.chunk = attn_chunk_for(f16, dh);
     w.nchunk_max = (n_cap + w.chunk - 1) / w.chunk;
-    w.fused = w.nchunk_max <= kFuseMaxChunks;
+    w.fused = w.nchunk_max <= kFuseMaxChunks && B <= kMaxBatch;
     w.q = A.take<float>((size_t)B * c * dh);
     w.part = A.take<float>((size_t)B * c * w.nchunk_max * (dh + 2));
     w.H = A.take<float>((size_t)B * c * dh);
     const int nch = axpy_chunks(cap * dh, d, f16, w.fused ? dh : 0, &w.rpc);
     w.partial = A.take<float>((size_t)nch * B * d);
+    w.mf = plan_mfma(A, B, d, mfma_floats(B, (long long)cap * 3 * dh));
     return w;
 }
 
@@ -186,8 +219,9 @@ struct LayerWs {
     float2* sm;                       // statistics of x'
     int32_t* idxA[2]; int32_t* cntA[2];
     int32_t* idxM[2]; int32_t* cntM[2];
-    MhaWs mha; MlpWs mlp;             // main-stream scratch
-    PredWs predA, predM;              // predictor-stream scratch
+    MhaWs mha; MlpWs mlp;             // attention and MLP scratch
+    PredWs predA, predM;              // predictor scratch
+    MfmaWs mf;                        // matrix-core scratch of every launch of the layer
     int tiles;                        // LayerNorm statistic slices per row
 };
 LayerWs plan_layer(Arena& A, const djv_model& m, bool dense) {
@@ -212,11 +246,15 @@ LayerWs plan_layer(Arena& A, const djv_model& m, bool dense) {
     w.mha = plan_mha(A, m.B, m.d, m.dh, capA, m.n_cap, f16);
     w.mlp = plan_mlp(A, m.B, m.d, capM, f16);
     if (!dense) {
-        w.predA = plan_predict(A, m.B, m.r, m.h, true);
-        w.predM = plan_predict(A, m.B, m.r, m.N, true);
+        w.predA = plan_predict(A, m.B, m.d, m.r, m.h, true);
+        w.predM = plan_predict(A, m.B, m.d, m.r, m.N, true);
     } else {
-        w.predA = w.predM = PredWs{nullptr, nullptr, nullptr};
+        w.predA = w.predM = PredWs{nullptr, nullptr, nullptr, MfmaWs{nullptr, nullptr}};
     }
+    // the layer's largest launches: Q/K/V with both P1, both P2, MLP up
+    const long long rows = std::max({(long long)capA * 3 * m.dh + 2LL * m.r, (long long)m.h + m.N,
+                                     (long long)capM});
+    w.mf = plan_mfma(A, m.B, std::max(m.d, m.r), mfma_floats(m.B, rows));
     return w;
 }
 
@@ -274,9 +312,10 @@ GemvSeg seg_up(const void* W1, const void* b1, const UnitList& neurons, const Ro
     return S;
 }
 
-GemvArgs gemv_args(int cols, int B, int prof) {
+GemvArgs gemv_args(int cols, int B, int prof, const MfmaWs& mf) {
     GemvArgs g{};
     g.cols = cols; g.B = B; g.flags = device_flags(); g.prof = prof;
+    g.yh = mf.yh; g.mfma_part = mf.part;
     return g;
 }
 void add_seg(GemvArgs& g, const GemvSeg& S) { g.seg[g.nseg++] = S; }
@@ -285,11 +324,11 @@ void add_side(GemvArgs& g, const SelectJob& J) { g.side[g.nside++] = J; }
 // One or two predictors reading the same input, in three launches: both first layers
 // (one GEMV launch), both second layers (one launch), both selections (one launch).
 djv_status run_predict(bool f16, int B, int d, int r, const RowInput& in, const PredJob* jobs,
-                       int njobs, hipStream_t s) {
-    GemvArgs g = gemv_args(d, B, DJV_PROF_PRED_1);
+                       int njobs, const MfmaWs& mf, hipStream_t s) {
+    GemvArgs g = gemv_args(d, B, DJV_PROF_PRED_1, mf);
     for (int i = 0; i < njobs; ++i) add_seg(g, seg_first(jobs[i], r, in));
     DJV_HIP(launch_gemv(f16, g, s));
-    g = gemv_args(r, B, DJV_PROF_PRED_2);
+    g = gemv_args(r, B, DJV_PROF_PRED_2, mf);
     for (int i = 0; i < njobs; ++i) add_seg(g, seg_second(jobs[i]));
     DJV_HIP(launch_gemv(f16, g, s));
     SelectJob sj[2];
@@ -317,7 +356,7 @@ djv_status run_mlp(bool f16, int B, int d, int N, const RowInput& in, const void
                    int cap, const float* resid, float* out, float2* stats, const MlpWs& w,
                    hipStream_t s) {
     const UnitList list{idx, count, cap, N};
-    GemvArgs g = gemv_args(d, B, DJV_PROF_MLP_UP);
+    GemvArgs g = gemv_args(d, B, DJV_PROF_MLP_UP, w.mf);
     add_seg(g, seg_up(W1, b1, list, in, w.a));
     DJV_HIP(launch_gemv(f16, g, s));
     return run_down(f16, B, d, W2, list, resid, out, stats, w, s);
@@ -365,7 +404,7 @@ djv_status run_mha(bool f16, int B, int d, int h, int dh, int n, int n_cap, cons
                    const int32_t* count, int cap, float scale, const float* resid, float* out,
                    float2* stats, const MhaWs& w, hipStream_t s) {
     const UnitList heads{idx, count, cap, h};
-    GemvArgs g = gemv_args(d, B, DJV_PROF_QKV);
+    GemvArgs g = gemv_args(d, B, DJV_PROF_QKV, w.mf);
     g.Kc = Kc; g.Vc = Vc; g.h = h; g.dh = dh; g.n = n; g.n_cap = n_cap;
     add_seg(g, seg_qkv(Wqkv, heads, dh, in, w.q));
     DJV_HIP(launch_gemv(f16, g, s));
@@ -379,6 +418,7 @@ djv_status check_model(const djv_model* m) {
     DJV_TRY(check_batch(m->B));
     DJV_TRY(check_rowlen(m->d, m->wt, "d"));
     DJV_TRY(check_rowlen(m->r, m->wt, "r"));
+    DJV_TRY(check_wide_batch(m->B, m->wt, {m->d, m->r}));
     DJV_REQUIRE(m->N >= 1 && m->h >= 1, DJV_EINVAL, "N and h must be >= 1");
     DJV_REQUIRE(m->dh == 64 || m->dh == 128, DJV_EUNSUPPORTED, "dh must be 64 or 128 (got %d)", m->dh);
     DJV_REQUIRE(m->n >= 0 && m->n < m->n_cap, DJV_EINVAL, "need 0 <= n < n_cap (n = %d, n_cap = %d)", m->n, m->n_cap);
@@ -495,7 +535,7 @@ djv_status layer_body(const djv_model& m, const djv_layer& L, const LayerIO& io,
     const RowInput in_m = ln_input(w.xm, w.sm, w, m.eps);
     if (serial) {
         const PredJob jm = job_M(m, L, w, buf, tr, l);
-        DJV_TRY(run_predict(f16, m.B, m.d, m.r, in_m, &jm, 1, s));
+        DJV_TRY(run_predict(f16, m.B, m.d, m.r, in_m, &jm, 1, w.mf, s));
     }
     DJV_TRY(run_mlp(f16, m.B, m.d, m.N, in_m, L.W1, L.b1, L.W2, w.idxM[buf], count_of(m, w.cntM[buf]),
                     cap_of(m.mode, m.k_M, m.N, m.B), w.xm, io.x_out, io.s_out, w.mlp, s));
@@ -507,7 +547,7 @@ djv_status serial_layer(const djv_model& m, const djv_layer& L, const LayerIO& i
                         const LayerWs& w, const djv_trace* tr, int l, hipStream_t s) {
     DJV_TRY(trace_x(tr, m, l, io.x_in, s));
     const PredJob ja = job_A(m, L, w, 0, tr, l);
-    DJV_TRY(run_predict(m.wt == DJV_F16, m.B, m.d, m.r, ln_input(io.x_in, io.s_in, w, m.eps), &ja, 1, s));
+    DJV_TRY(run_predict(m.wt == DJV_F16, m.B, m.d, m.r, ln_input(io.x_in, io.s_in, w, m.eps), &ja, 1, w.mf, s));
     DJV_TRY(layer_body(m, L, io, w, 0, true, tr, l, s));
     return trace_sets(tr, m, l, w, 0, s);
 }
@@ -536,7 +576,7 @@ djv_status dejavu_workspace_bytes(int B, int d, int N, int h, int dh, int r, int
         const int n_out = N > h ? N : h;
         if (n_out > 0) {
             Arena a(nullptr);
-            plan_predict(a, Bq, r, n_out, true);
+            plan_predict(a, Bq, d, r, n_out, true);
             upd(a.off);
         }
         if (N > 0 && d > 0) {
@@ -602,6 +642,7 @@ djv_status dejavu_predict(djv_dtype wt, int B, int d, int r, int n_out, const fl
     DJV_TRY(check_batch(B));
     DJV_TRY(check_rowlen(d, wt, "d"));
     DJV_TRY(check_rowlen(r, wt, "r"));
+    DJV_TRY(check_wide_batch(B, wt, {d, r}));
     DJV_TRY(check_select(n_out, mode, k, t, "predict"));
     DJV_TRY(check_ptr(y, "y"));
     DJV_TRY(check_ptr(P1, "P1"));
@@ -610,12 +651,12 @@ djv_status dejavu_predict(djv_dtype wt, int B, int d, int r, int n_out, const fl
     DJV_TRY(check_idx_ptr(count, "count"));
     DJV_TRY(check_opt_ptr(logits, "logits"));
     Arena sz(nullptr);
-    plan_predict(sz, B, r, n_out, logits == nullptr);
+    plan_predict(sz, B, d, r, n_out, logits == nullptr);
     DJV_TRY(check_ws(ws, ws_bytes, sz.off));
     Arena A(ws);
-    const PredWs w = plan_predict(A, B, r, n_out, logits == nullptr);
+    const PredWs w = plan_predict(A, B, d, r, n_out, logits == nullptr);
     const PredJob j{P1, P2, n_out, (int)mode, k, t, idx, count, logits ? logits : w.z, &w};
-    return run_predict(wt == DJV_F16, B, d, r, plain_input(y), &j, 1, (hipStream_t)stream);
+    return run_predict(wt == DJV_F16, B, d, r, plain_input(y), &j, 1, w.mf, (hipStream_t)stream);
 }
 
 static djv_status mlp_common(djv_dtype wt, int B, int d, int N, const float* y, const void* W1,
@@ -625,6 +666,7 @@ static djv_status mlp_common(djv_dtype wt, int B, int d, int N, const float* y, 
     DJV_TRY(check_dtype(wt));
     DJV_TRY(check_batch(B));
     DJV_TRY(check_rowlen(d, wt, "d"));
+    DJV_TRY(check_wide_batch(B, wt, {d}));
     DJV_REQUIRE(N >= 1, DJV_EINVAL, "N must be >= 1");
     DJV_REQUIRE(cap >= 1 && cap <= N, DJV_EINVAL, "cap = %d outside [1, N = %d]", cap, N);
     DJV_TRY(check_ptr(y, "y"));
@@ -667,6 +709,7 @@ static djv_status mha_common(djv_dtype wt, int B, int d, int h, int dh, int n, i
     DJV_TRY(check_dtype(wt));
     DJV_TRY(check_batch(B));
     DJV_TRY(check_rowlen(d, wt, "d"));
+    DJV_TRY(check_wide_batch(B, wt, {d}));
     DJV_REQUIRE(h >= 1, DJV_EINVAL, "h must be >= 1");
     DJV_REQUIRE(dh == 64 || dh == 128, DJV_EUNSUPPORTED, "dh must be 64 or 128 (got %d)", dh);
     DJV_REQUIRE(n >= 0 && n < n_cap, DJV_EINVAL, "need 0 <= n < n_cap (n = %d, n_cap = %d)", n, n_cap);
@@ -772,11 +815,11 @@ djv_status dejavu_stack_decode(const djv_model* m, const djv_layer* layers, int 
         const LayerIO io0 = layer_io(x, w, 0, L);
         const RowInput in0 = ln_input(io0.x_in, io0.s_in, w, m->eps);
         const PredJob ja = job_A(*m, layers[0], w, 0, trace, 0), jm = job_M(*m, layers[0], w, 0, trace, 0);
-        GemvArgs g = gemv_args(m->d, m->B, DJV_PROF_PRED_1);
+        GemvArgs g = gemv_args(m->d, m->B, DJV_PROF_PRED_1, w.mf);
         add_seg(g, seg_first(ja, m->r, in0));
         add_seg(g, seg_first(jm, m->r, in0));
         DJV_HIP(launch_gemv(f16, g, sm));
-        g = gemv_args(m->r, m->B, DJV_PROF_PRED_2);
+        g = gemv_args(m->r, m->B, DJV_PROF_PRED_2, w.mf);
         add_seg(g, seg_second(ja));
         add_seg(g, seg_second(jm));
         DJV_HIP(launch_gemv(f16, g, sm));
@@ -799,7 +842,7 @@ djv_status dejavu_stack_decode(const djv_model* m, const djv_layer* layers, int 
         DJV_TRY(trace_x(trace, *m, l, io.x_in, sm));
 
         // Q/K/V of the kept heads (+ K/V append), P1 of both predictors for l+1, S_M^l
-        GemvArgs g = gemv_args(m->d, m->B, DJV_PROF_QKV);
+        GemvArgs g = gemv_args(m->d, m->B, DJV_PROF_QKV, w.mf);
         g.Kc = Ly.Kc; g.Vc = Ly.Vc; g.h = m->h; g.dh = m->dh; g.n = m->n; g.n_cap = m->n_cap;
         add_seg(g, seg_qkv(Ly.Wqkv, heads, m->dh, in_a, w.mha.q));
         if (ahead) {
@@ -812,7 +855,7 @@ djv_status dejavu_stack_decode(const djv_model* m, const djv_layer* layers, int 
 
         if (ahead && w.mha.fused) {
             // P2 of both predictors for l+1, with the attention chunks in its first blocks
-            g = gemv_args(m->r, m->B, DJV_PROF_PRED_2);
+            g = gemv_args(m->r, m->B, DJV_PROF_PRED_2, w.mf);
             add_seg(g, seg_second(na));
             add_seg(g, seg_second(nm));
             g.attn = attend_args(m->B, m->h, m->dh, m->n, m->n_cap, Ly.Kc, Ly.Vc, heads, m->scale, w.mha);
@@ -822,7 +865,7 @@ djv_status dejavu_stack_decode(const djv_model* m, const djv_layer* layers, int 
             DJV_TRY(run_attend(f16, m->B, m->h, m->dh, m->n, m->n_cap, Ly.Kc, Ly.Vc, heads, m->scale,
                                w.mha, sm));
             if (ahead) {
-                g = gemv_args(m->r, m->B, DJV_PROF_PRED_2);
+                g = gemv_args(m->r, m->B, DJV_PROF_PRED_2, w.mf);
                 add_seg(g, seg_second(na));
                 add_seg(g, seg_second(nm));
                 DJV_HIP(launch_gemv(f16, g, sm));
@@ -833,7 +876,7 @@ djv_status dejavu_stack_decode(const djv_model* m, const djv_layer* layers, int 
             DJV_TRY(copy_async(trace->x_mid + (size_t)l * m->B * m->d, w.xm, (size_t)m->B * m->d * 4, sm));
 
         // MLP up-projection of the kept neurons, S_A^{l+1}
-        g = gemv_args(m->d, m->B, DJV_PROF_MLP_UP);
+        g = gemv_args(m->d, m->B, DJV_PROF_MLP_UP, w.mf);
         add_seg(g, seg_up(Ly.W1, Ly.b1, neurons, ln_input(w.xm, w.sm, w, m->eps), w.mlp.a));
         if (ahead) add_side(g, select_job(na));
         DJV_HIP(launch_gemv(f16, g, sm));

@@ -253,8 +253,150 @@ __global__ __launch_bounds__(kFinGroups * kFinQuads) void axpy_finalize_kernel(A
     }
 }
 
+// ---------------------------------------------------------------------------------
+// Batches of more than kMaxBatch rows (fp16 weights): the same partial tiles, computed on
+// the matrix cores.  D[b, c] = sum_r coef[b, r] W[r, c] over the block's rows is
+// v_mfma_f32_16x16x32_f16 with A = coefficients (rounded to fp16) and B = weights.  The
+// instruction wants 8 consecutive k (here: rows) per lane for one column, so each 32-row x
+// 64-column weight tile is staged through LDS: coalesced 16-byte row loads in, 16-bit
+// column reads out.  A block owns 64 columns (4 waves x 16) and a chunk of rows; the tiles
+// of a chunk are loaded kPrefetch at a time, one 16-byte load per thread per tile.
+// ---------------------------------------------------------------------------------
+typedef _Float16 h8m_t __attribute__((ext_vector_type(8)));
+typedef float f4m_t __attribute__((ext_vector_type(4)));
+constexpr int kMfmaCols = 64;
+constexpr int kMfmaRows = 32;
+constexpr int kPrefetch = 8;
+constexpr int kWtPitch = kMfmaCols + 8;  // halfs per LDS row (padding against bank conflicts)
+
+static __device__ const Vec16 g_zero16 = {};
+
+template <int BT>
+__global__ __launch_bounds__(kThreads) void axpy_mfma_kernel(AxpyArgs a) {
+    extern __shared__ float dyn[];  // [rpc] rows, then [BT * 16][rpc] fp16 coefficients
+    __shared__ _Float16 wt[kPrefetch][kMfmaRows][kWtPitch];
+    constexpr int BP = BT * 16;
+    const int tid = threadIdx.x, wv = tid / kWave, l = tid % kWave;
+    const int chunk = blockIdx.y;
+    const int c0 = blockIdx.x * kMfmaCols;
+    const int count = read_count(a.list, a.flags);
+    const int rows = count * a.rpu;
+    const int r0 = chunk * a.rows_per_chunk;
+    if (r0 >= rows) return;
+    const int nr = min(rows, r0 + a.rows_per_chunk) - r0;
+    int* row_s = reinterpret_cast<int*>(dyn);
+    _Float16* cf_s = reinterpret_cast<_Float16*>(dyn + a.rows_per_chunk);
+    for (int i = tid; i < a.rows_per_chunk; i += kThreads) {
+        int row = -1;
+        if (i < nr) {
+            const int r = r0 + i;
+            const int u = r / a.rpu, sub = r - u * a.rpu;
+            const int unit = unit_of(a.list, u, a.flags);
+            row = unit < 0 ? -1 : unit * a.rpu + sub;
+        }
+        row_s[i] = row;
+        for (int b = 0; b < BP; ++b)
+            cf_s[b * a.rows_per_chunk + i] =
+                (_Float16)((row >= 0 && b < a.B) ? a.coef[(size_t)b * a.ldc + r0 + i] : 0.f);
+    }
+    __syncthreads();
+
+    // loads: thread t moves row t / 8, columns 8 (t % 8) .. + 8 of a tile
+    const int lr = tid / 8, lc = 8 * (tid % 8);
+    const bool col_ok = c0 + lc + 8 <= a.cols;
+    const char* Wb = reinterpret_cast<const char*>(a.W);
+    const size_t row_bytes = (size_t)a.cols * 2;
+    auto load_tile = [&](int t) -> Vec16 {
+        const int i = t * kMfmaRows + lr;
+        const int row = i < nr ? row_s[i] : -1;
+        const char* p = (row >= 0 && col_ok) ? Wb + (size_t)row * row_bytes + (size_t)(c0 + lc) * 2
+                                             : reinterpret_cast<const char*>(&g_zero16);
+        return ldg16_nt(p);
+    };
+    const int ntiles = (nr + kMfmaRows - 1) / kMfmaRows;
+    f4m_t acc[BT];
+#pragma unroll
+    for (int t = 0; t < BT; ++t) acc[t] = f4m_t{0.f, 0.f, 0.f, 0.f};
+    const int col = wv * 16 + l % 16, kb = 8 * (l / 16);
+    Vec16 cur[kPrefetch];
+#pragma unroll
+    for (int q = 0; q < kPrefetch; ++q) cur[q] = load_tile(min(q, ntiles - 1));
+    for (int t0 = 0; t0 < ntiles; t0 += kPrefetch) {
+#pragma unroll
+        for (int q = 0; q < kPrefetch; ++q) *reinterpret_cast<Vec16*>(&wt[q][lr][lc]) = cur[q];
+        __syncthreads();
+        // the next tiles' loads go out before this group's products
+#pragma unroll
+        for (int q = 0; q < kPrefetch; ++q) cur[q] = load_tile(min(t0 + kPrefetch + q, ntiles - 1));
+#pragma unroll
+        for (int q = 0; q < kPrefetch; ++q) {
+            if (t0 + q >= ntiles) break;
+            h8m_t bw;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bw[e] = wt[q][kb + e][col];
+            const int rbase = (t0 + q) * kMfmaRows + kb;
+#pragma unroll
+            for (int t = 0; t < BT; ++t) {
+                const _Float16* cp = cf_s + (16 * t + l % 16) * a.rows_per_chunk + rbase;
+                h8m_t av;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) av[e] = rbase + e < a.rows_per_chunk ? cp[e] : (_Float16)0.f;
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bw, acc[t], 0, 0, 0);
+            }
+        }
+        __syncthreads();
+    }
+    // lane l holds D[b = 16 t + 4 (l / 16) + q][column wv * 16 + l % 16]
+    const int c = c0 + col;
+    if (c < a.cols) {
+#pragma unroll
+        for (int t = 0; t < BT; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int b = 16 * t + 4 * (l / 16) + q;
+                if (b < a.B) a.partial[((size_t)chunk * a.B + b) * a.cols + c] = acc[t][q];
+            }
+    }
+}
+
+template <typename T>
+hipError_t dispatch_mfma(const AxpyArgs& a, hipStream_t s) {
+    if (a.B > 32 || a.attn_part) return hipErrorInvalidValue;
+    const int rows_cap = a.list.cap * a.rpu;
+    const int nch = rows_cap > 0 ? (rows_cap + a.rows_per_chunk - 1) / a.rows_per_chunk : 0;
+    if (nch > 0) {
+        const int bt = a.B <= 16 ? 1 : 2;
+        const size_t dyn = (size_t)a.rows_per_chunk * (bt * 16 * 2 + sizeof(int));
+        // chunks of up to kAxpyMaxChunkRows rows take more than 64 KiB of LDS in all
+        static const hipError_t opt_in = [] {
+            const int most = 160 * 1024 - (int)sizeof(_Float16) * kPrefetch * kMfmaRows * kWtPitch;
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&axpy_mfma_kernel<1>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, most);
+            if (e == hipSuccess)
+                e = hipFuncSetAttribute(reinterpret_cast<const void*>(&axpy_mfma_kernel<2>),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, most);
+            return e;
+        }();
+        if (opt_in != hipSuccess) return opt_in;
+        dim3 grid((a.cols + kMfmaCols - 1) / kMfmaCols, nch);
+        prof_begin(a.prof, s);
+        if (bt == 1) hipLaunchKernelGGL(axpy_mfma_kernel<1>, grid, dim3(kThreads), dyn, s, a);
+        else hipLaunchKernelGGL(axpy_mfma_kernel<2>, grid, dim3(kThreads), dyn, s, a);
+        prof_end(a.prof, s);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    dim3 fgrid((a.cols + kLnTile - 1) / kLnTile, a.B);
+    hipLaunchKernelGGL(axpy_finalize_kernel, fgrid, dim3(kFinGroups * kFinQuads), 0, s, a);
+    return hipGetLastError();
+}
+
 template <typename T>
 hipError_t dispatch(const AxpyArgs& a, hipStream_t s) {
+    if (a.B > kMaxBatch) {
+        if constexpr (sizeof(T) == 2) return dispatch_mfma<T>(a, s);
+        else return hipErrorInvalidValue;
+    }
     constexpr int E = WTraits<T>::kPerVec;
     const int tiles = (a.cols / E + kWave - 1) / kWave;
     const int rows_cap = a.list.cap * a.rpu;
@@ -285,7 +427,8 @@ hipError_t dispatch(const AxpyArgs& a, hipStream_t s) {
 
 int axpy_chunks(int rows_cap, int cols, bool f16, int max_rows_per_chunk, int* rows_per_chunk) {
     const int E = f16 ? 8 : 4;
-    const int tiles = (cols / E + kWave - 1) / kWave;
+    const int tiles = (cols / E + kWave - 1) / kWave;  // 512-column tiles (the matrix-core
+                                                       // form uses 64-column tiles, 8 per tile)
     const int step = kWavesPerBlock * kUnroll;  // 32 rows: one pass of the block
     if (rows_cap <= 0) {
         *rows_per_chunk = step;

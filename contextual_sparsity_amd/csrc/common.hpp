@@ -6,10 +6,13 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "dejavu.h"
+
 namespace djv {
 
 constexpr int kWave = 64;          // CDNA wavefront width
-constexpr int kMaxBatch = 4;       // batch rows held in registers by the GEMV kernels
+constexpr int kMaxBatch = DJV_MAX_VALU_BATCH;  // batch rows held in registers by the vector-ALU kernels
+constexpr int kMaxBatchMfma = DJV_MAX_BATCH;   // batch rows of the matrix-core kernels (fp16 weights)
 constexpr unsigned kFlagBadIndex = 1u;
 constexpr unsigned kFlagBadCount = 2u;
 
@@ -288,11 +291,19 @@ struct GemvArgs {
     // selections and the GEMV segments; independent of both
     AttnArgs attn;
     int nattn;
+    // batches above kMaxBatch (matrix-core form): fp16 activation copies [seg][32, cols]
+    // and the k-slice partials (workspace, sized by mfma_shape)
+    __half* yh;
+    float* mfma_part;
     unsigned* flags;
     int prof;             // profiling family of this launch (0: none)
 };
 
 hipError_t launch_gemv(bool f16, const GemvArgs& a, hipStream_t s);
+// Matrix-core form for B > kMaxBatch (fp16 weights, cols % 32 == 0): k-slices and the
+// partial floats a launch needs.
+void mfma_shape(const GemvArgs& a, int* slices, long long* floats);
+hipError_t launch_gemv_mfma(const GemvArgs& a, __half* Yh, float* partial, hipStream_t s);
 
 struct AxpyArgs {
     const void* W;        // [units*rpu, cols] weights

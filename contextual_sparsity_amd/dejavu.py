@@ -19,7 +19,8 @@ DJV_OK, DJV_EINVAL, DJV_EALIGN, DJV_EWORKSPACE, DJV_EUNSUPPORTED, DJV_EHIP = 0, 
 DJV_F32, DJV_F16 = 0, 1
 DJV_TOPK, DJV_THRESHOLD = 0, 1
 DJV_FLAG_BAD_INDEX, DJV_FLAG_BAD_COUNT = 1, 2
-DJV_MAX_BATCH = 4
+DJV_MAX_BATCH = 32
+DJV_MAX_VALU_BATCH = 4
 
 STATUS_NAMES = {0: "DJV_OK", -1: "DJV_EINVAL", -2: "DJV_EALIGN", -3: "DJV_EWORKSPACE",
                 -4: "DJV_EUNSUPPORTED", -5: "DJV_EHIP"}

@@ -71,8 +71,13 @@ typedef enum {
 /* Limits of this build (DJV_EUNSUPPORTED beyond them):
  *   B <= DJV_MAX_BATCH; d and r multiples of 8 with d*esize <= 32768 bytes and
  *   r*esize <= 32768 bytes (one row fits 256 threads x 8 x 16-byte loads); dh in {64, 128};
- *   n_out <= 65536 for selection. */
-#define DJV_MAX_BATCH 4
+ *   n_out <= 65536 for selection.
+ *   Batches of B <= DJV_MAX_VALU_BATCH rows run on the vector ALU in either dtype.  Larger
+ *   batches run their products on the matrix cores and need DJV_F16 weights and every
+ *   GEMV row length (d, and r for the predictor) a multiple of 32; their fp16 rounding of
+ *   the normalised activations (and of the row-axpy coefficients) is part of the result. */
+#define DJV_MAX_BATCH 32
+#define DJV_MAX_VALU_BATCH 4
 
 /* --------------------------------------------------------------------------------------
  * dejavu_workspace_bytes -- workspace size for any call with these dimensions or smaller.

@@ -91,7 +91,11 @@ def test_predict_argument_errors():
         return _status(p, **a)
     assert call(wt=5) == dj.DJV_EINVAL
     assert call(B=0) == dj.DJV_EINVAL
-    assert call(B=5) == dj.DJV_EUNSUPPORTED
+    assert call(B=dj.DJV_MAX_BATCH + 1) == dj.DJV_EUNSUPPORTED
+    # batches above the vector-ALU limit need fp16 weights and row lengths divisible by 32
+    assert call(B=5, wt=dj.DJV_F32) == dj.DJV_EUNSUPPORTED
+    assert call(B=5, d=776) == dj.DJV_EUNSUPPORTED
+    assert call(B=5, r=136) == dj.DJV_EUNSUPPORTED
     assert call(d=100) == dj.DJV_EINVAL
     assert call(d=20000) == dj.DJV_EUNSUPPORTED
     assert call(r=0) == dj.DJV_EINVAL
@@ -119,6 +123,8 @@ def test_mlp_argument_errors():
     assert call(resid=MIS) == dj.DJV_EALIGN
     assert call(out=None) == dj.DJV_EINVAL
     assert call(N=0) == dj.DJV_EINVAL
+    assert call(B=6) == dj.DJV_EUNSUPPORTED  # fp32 weights stay on the vector ALU
+    assert call(B=6, wt=dj.DJV_F16, d=776) == dj.DJV_EUNSUPPORTED
     assert call(ws=(A, 1024)) == dj.DJV_EWORKSPACE
     assert _status(dj.dejavu_dense_mlp, dj.DJV_F32, 1, 768, 3072, A, A, A, A, None, A, (A, 1024)) \
         == dj.DJV_EWORKSPACE
@@ -141,6 +147,8 @@ def test_mha_argument_errors():
     assert call(Kc=None) == dj.DJV_EINVAL
     assert call(Vc=MIS) == dj.DJV_EALIGN
     assert call(head_idx=None) == dj.DJV_EINVAL
+    assert call(B=33) == dj.DJV_EUNSUPPORTED
+    assert call(B=8, d=776) == dj.DJV_EUNSUPPORTED
     assert call(ws=(A, 64)) == dj.DJV_EWORKSPACE
 
 
@@ -157,6 +165,10 @@ def test_layer_and_stack_argument_errors():
     assert _status(dj.dejavu_sparse_layer, bad, L, A, None, WS) == dj.DJV_EINVAL
     bad = dj.make_model(dj.DJV_F16, 1, 768, 3072, 12, 64, 128, 128, 129, 0.125, eps=0.0)
     assert _status(dj.dejavu_sparse_layer, bad, L, A, None, WS) == dj.DJV_EINVAL
+    bad = dj.make_model(dj.DJV_F16, 16, 768, 3072, 12, 64, 136, 128, 129, 0.125)
+    assert _status(dj.dejavu_sparse_layer, bad, L, A, None, WS) == dj.DJV_EUNSUPPORTED
+    bad = dj.make_model(dj.DJV_F32, 16, 768, 3072, 12, 64, 128, 128, 129, 0.125)
+    assert _status(dj.dejavu_sparse_layer, bad, L, A, None, WS) == dj.DJV_EUNSUPPORTED
     L2 = dj.make_layer(w, dict(p, P2_M=None))
     assert _status(dj.dejavu_sparse_layer, m, L2, A, None, WS) == dj.DJV_EINVAL
     assert _status(dj.dejavu_stack_decode, m, [L, L2], A, True, False, None, WS) == dj.DJV_EINVAL

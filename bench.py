@@ -4,15 +4,20 @@
 A step is one decode token through a stack of OPT-175B-shaped layers (d 12288, 49152
 neurons, 96 heads of 128, 2048 cached positions, predictor width 1024, fp16 weights,
 batch 1): per layer LayerNorm, the two sparsity predictors and top-k selection (5% of
-neurons, 20% of heads; layer l+1's sets predicted on a second stream while layer l
-runs), head-sparse Q/K/V with the KV append, attention over the kept heads, the
-head-sparse output projection, LayerNorm, and the sparse MLP.  Every layer has its own
-weights and cache, all resident in HBM before timing starts.
+neurons, 20% of heads; layer l+1's sets predicted inside layer l's launches),
+head-sparse Q/K/V with the KV append, attention over the kept heads, the head-sparse
+output projection, LayerNorm, and the sparse MLP.  Every layer has its own weights and
+cache, all resident in HBM before timing starts.
 
 Prints one JSON line: HBM GB/s on the bytes the step touches (the value), microseconds
 per layer, the dense path on the same stack, the roofline of the dominant kernel
 (head-sparse Q/K/V GEMV) measured with HIP events around its launches, and the CPU
 oracle timed on a bounded sample of the same workload.
+
+--sweep instead times OPT-175B-shaped layers over neuron keep-percentages
+{1..100}, head keep-percentages {10..100} and batches {1..32} (union index sets),
+with the vector-ALU and the matrix-core kernel forms where both apply and the dense path
+per batch, and prints one JSON line per point.
 """
 from __future__ import annotations
 
@@ -69,6 +74,10 @@ def parse(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget")
     ap.add_argument("--breakdown", action="store_true", help="time every kernel family")
     ap.add_argument("--no-lookahead", action="store_true")
+    ap.add_argument("--sweep", action="store_true", help="the keep-percentage x batch sweep")
+    ap.add_argument("--sweep-layers", type=int, default=8, help="distinct layers per sweep step")
+    ap.add_argument("--sweep-steps", type=int, default=5)
+    ap.add_argument("--sweep-batches", default="", help="comma list overriding the sweep's batches")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 1 GiB three times (reference for HBM byte "
                          "counters) and exit")
@@ -137,12 +146,106 @@ def cpu_baseline(wl, s, layers_gpu, preds_gpu, x0, k_A, k_M, budget_s, lb):
     }
 
 
+# ------------------------------------------------------------------------ sparsity x batch sweep
+def union_bytes(s, B, uA, uM):
+    """Bytes a layer touches with union sets of uA heads and uM neurons at batch B."""
+    e = 2 if s.dtype == "f16" else 4
+    pred = (2 * s.d * s.r + s.r * s.N + s.r * s.h) * e
+    return pred + 4 * s.d * s.dh * uA * e + B * 2 * (s.n + 1) * s.dh * uA * e + 2 * uM * s.d * e + uM * e
+
+
+def sweep(args) -> int:
+    import torch
+    from contextual_sparsity_amd import configs, synth
+    from contextual_sparsity_amd import dejavu as dj
+
+    base = configs.WORKLOADS["opt175b-1layer-fp16"]
+    batches = [int(b) for b in args.sweep_batches.split(",")] if args.sweep_batches else \
+        list(configs.SWEEP_BATCH)
+    Bmax = max(batches)
+    L = args.sweep_layers
+    s = base.shape.with_(B=Bmax)
+    dev = "cuda"
+    t0 = time.time()
+    layers = [synth.make_layer(s, args.seed, l, dev) for l in range(L)]
+    preds = [synth.make_predictors(s, args.seed, l, dev) for l in range(L)]
+    torch.cuda.synchronize()
+    log(f"sweep: {L} OPT-175B-shaped layers with caches for {Bmax} sequences "
+        f"({time.time() - t0:.1f} s, {torch.cuda.memory_allocated() / 2**30:.1f} GiB)")
+    desc = [dj.make_layer(layers[l], preds[l]) for l in range(L)]
+    big = dj.make_model(dj.DJV_F16, Bmax, s.d, s.N, s.h, s.dh, s.r, s.n, s.cap, base.scale, dj.DJV_TOPK,
+                        s.h, s.N)
+    ws = dj.workspace(max(dj.dejavu_workspace_bytes_model(big),
+                          dj.dejavu_workspace_bytes_model(dj.make_model(
+                              dj.DJV_F16, Bmax, s.d, s.N, s.h, s.dh, s.r, s.n, s.cap, base.scale))), dev)
+    stream = torch.cuda.current_stream()
+    counts = torch.zeros(L, 2, dtype=torch.int32, device=dev)
+    trace = dj.make_trace(counts=counts)
+    default_min = dj.dejavu_set_mfma_min_batch(dj.DJV_MAX_VALU_BATCH + 1)
+
+    def run(m, x, x0, dense, n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(2):
+            x.copy_(x0)
+            dj.dejavu_stack_decode(m, desc, x, True, dense, None, ws, stream)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(n):
+            x.copy_(x0)
+            dj.dejavu_stack_decode(m, desc, x, True, dense, None, ws, stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / n / L
+
+    rows = []
+    for B in batches:
+        sb = s.with_(B=B)
+        x0 = synth.make_input(sb, args.seed, dev)
+        x = x0.clone()
+        m_dense = dj.make_model(dj.DJV_F16, B, s.d, s.N, s.h, s.dh, s.r, s.n, s.cap, base.scale)
+        forms = ["valu", "mfma"] if B <= dj.DJV_MAX_VALU_BATCH else ["mfma"]
+        dense_us = {}
+        for form in forms:
+            dj.dejavu_set_mfma_min_batch(1 if form == "mfma" else dj.DJV_MAX_VALU_BATCH + 1)
+            dense_us[form] = run(m_dense, x, x0, True, max(2, args.sweep_steps // 2))
+        for pA in configs.SWEEP_PCT_A:
+            for pM in configs.SWEEP_PCT_M:
+                kA, kM = configs.keep(pA, s.h), configs.keep(pM, s.N)
+                m = dj.make_model(dj.DJV_F16, B, s.d, s.N, s.h, s.dh, s.r, s.n, s.cap, base.scale,
+                                  dj.DJV_TOPK, kA, kM)
+                # union sizes of this point (the sets do not depend on the kernel form)
+                x.copy_(x0)
+                dj.dejavu_stack_decode(m, desc, x, True, False, trace, ws, stream)
+                c = counts.cpu().numpy().astype(float)
+                uA, uM = float(c[:, 0].mean()), float(c[:, 1].mean())
+                nbytes = union_bytes(s, B, uA, uM)
+                pt = {"batch": B, "pct_M": pM, "pct_A": pA, "k_M": kM, "k_A": kA,
+                      "union_M": round(uM, 1), "union_A": round(uA, 1),
+                      "bytes_per_layer": int(nbytes)}
+                for form in forms:
+                    dj.dejavu_set_mfma_min_batch(1 if form == "mfma" else dj.DJV_MAX_VALU_BATCH + 1)
+                    us = run(m, x, x0, False, args.sweep_steps)
+                    pt[f"{form}_us"] = round(us, 2)
+                    pt[f"{form}_GBps"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+                    pt[f"{form}_dense_us"] = round(dense_us[form], 2)
+                best = min(forms, key=lambda f: pt[f"{f}_us"])
+                pt["best"] = best
+                pt["speedup_vs_dense"] = round(min(dense_us.values()) / pt[f"{best}_us"], 3)
+                rows.append(pt)
+                print(json.dumps(pt), flush=True)
+    dj.dejavu_set_mfma_min_batch(default_min)
+    log(f"sweep done: {len(rows)} points")
+    return 0
+
+
 def main(argv=None) -> int:
     args = parse(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
               "multi-GPU path", file=sys.stderr)
         return 2
+    if args.sweep:
+        return sweep(args)
     import torch
     from contextual_sparsity_amd import configs, synth
     from contextual_sparsity_amd import dejavu as dj

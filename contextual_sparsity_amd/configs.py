@@ -63,3 +63,9 @@ WORKLOADS: Dict[str, Workload] = {
         "opt175b-1layer-fp16", LayerShape(d=12288, N=49152, h=96, dh=128, n=2048, r=1024),
         layers=1, pct_M=5, pct_A=20, lookahead=False),
 }
+
+# Sparsity and batch sweep on the OPT-175B layer shape: per-token keep-percentages of
+# neurons and heads crossed with the batch size (union index sets)
+SWEEP_PCT_M = (1, 2, 5, 10, 25, 50, 100)
+SWEEP_PCT_A = (10, 20, 50, 100)
+SWEEP_BATCH = (1, 2, 4, 8, 16, 32)

@@ -7,6 +7,7 @@
 #include "dejavu.h"
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <initializer_list>
 #include <cstdarg>
@@ -131,6 +132,18 @@ uint32_t tau_key(float t) {
     return score_key_host(tau);
 }
 
+// Batches of at least this many rows use the matrix-core kernels where they can (fp16
+// weights, row lengths divisible by 32); batches above kMaxBatch always do.
+std::atomic<int> g_mfma_min_batch{kMaxBatch + 1};
+
+bool wide_possible(int wt, std::initializer_list<int> cols) {
+    if (wt != DJV_F16) return false;
+    for (int c : cols)
+        if (c % 32 != 0) return false;
+    return true;
+}
+bool layer_wide(const djv_model& m) { return wide_possible(m.wt, {m.d, m.r}); }
+
 // ------------------------------------------------------------------------------------
 // Workspace plans.  The same functions size the workspace (base == nullptr) and carve
 // it, so a size query and a call always agree.
@@ -146,59 +159,73 @@ struct Arena {
     }
 };
 
-// Scratch of the matrix-core GEMV (batches above kMaxBatch): the fp16 activation copies and
-// the k-slice partials.  A launch over R weight rows in T 16-row tiles takes S slices, S
-// doubling while T * S < 2048, so S == 1 or T * S < 4096; its S * R * bpad partial floats
-// are then at most max(R, 4096 * 16) * bpad.  Plans size the partials by that bound on the
-// largest R of their launches, which holds whichever launch a schedule makes.
-struct MfmaWs { __half* yh; float* part; };
-long long mfma_floats(int B, long long max_rows) {
-    const long long bpad = B <= 16 ? 16 : 32;
-    return std::max(max_rows, 4096LL * 16) * bpad;
-}
-MfmaWs plan_mfma(Arena& A, int B, int max_cols, long long floats) {
-    if (B <= kMaxBatch) return MfmaWs{nullptr, nullptr};
-    MfmaWs w;
-    w.yh = A.take<__half>((size_t)kMaxSeg * kMaxBatchMfma * max_cols);
-    w.part = A.take<float>((size_t)floats);
+// Scratch of the matrix-core GEMV: its k-slice partials, sized for the largest launch a
+// plan makes (rows summed over the launch's segments, longest row).  `on` selects the
+// matrix-core form for every launch of a call; the scratch is reserved whenever the form
+// is possible (fp16 weights, row lengths divisible by 32), so a workspace size never
+// depends on the batch threshold in force.
+struct MfmaWs { float* part; bool on; bool reserved; };
+MfmaWs plan_mfma(Arena& A, bool possible, int B, long long max_rows, int max_cols) {
+    MfmaWs w{nullptr, false, false};
+    if (!possible) return w;
+    w.reserved = true;
+    w.part = A.take<float>((size_t)mfma_partial_floats(B, max_rows, max_cols));
+    w.on = B > kMaxBatch || B >= g_mfma_min_batch.load(std::memory_order_relaxed);
     return w;
 }
 
 struct PredWs { float* u; float* z; uint32_t* bits; MfmaWs mf; };
-PredWs plan_predict(Arena& A, int B, int d, int r, int n_out, bool need_z) {
+PredWs plan_predict(Arena& A, int B, int d, int r, int n_out, bool need_z, bool wide,
+                    const MfmaWs* shared = nullptr) {
     PredWs w;
     w.u = A.take<float>((size_t)B * r);
     w.z = need_z ? A.take<float>((size_t)B * n_out) : nullptr;
     w.bits = A.take<uint32_t>((size_t)B * words_of(n_out));
-    w.mf = plan_mfma(A, B, std::max(d, r), mfma_floats(B, std::max(r, n_out)));
+    w.mf = shared ? *shared : plan_mfma(A, wide, B, std::max(r, n_out), std::max(d, r));
     return w;
 }
 
 struct MlpWs { float* a; float* partial; int rpc; MfmaWs mf; };
-MlpWs plan_mlp(Arena& A, int B, int d, int cap, bool f16) {
+MlpWs plan_mlp(Arena& A, int B, int d, int cap, bool f16, bool wide, const MfmaWs* shared = nullptr) {
     MlpWs w;
     w.a = A.take<float>((size_t)B * (cap > 0 ? cap : 1));
-    const int nch = axpy_chunks(cap, d, f16, 0, &w.rpc);
+    int nch = axpy_chunks(cap, d, f16, 0, &w.rpc);
+    w.mf = shared ? *shared : plan_mfma(A, wide, B, cap, d);
+    if (w.mf.reserved) {
+        // room for either form's chunks; the rows per chunk of the form in use
+        int rpc_m = 0;
+        nch = std::max(nch, axpy_chunks_mfma(cap, d, &rpc_m));
+        if (w.mf.on) w.rpc = rpc_m;
+    }
     w.partial = A.take<float>((size_t)nch * B * d);
-    w.mf = plan_mfma(A, B, d, mfma_floats(B, cap));
     return w;
 }
 
 // fused: the O-projection merges the attention chunks itself (no merge kernel, no H);
 // possible when a head has at most kFuseMaxChunks chunks, with chunks of at most dh rows.
 struct MhaWs { float* q; float* part; float* H; float* partial; int rpc, chunk, nchunk_max; bool fused; MfmaWs mf; };
-MhaWs plan_mha(Arena& A, int B, int d, int dh, int cap, int n_cap, bool f16) {
+MhaWs plan_mha(Arena& A, int B, int d, int dh, int cap, int n_cap, bool f16, bool wide,
+              const MfmaWs* shared = nullptr) {
     MhaWs w;
     const int c = cap > 0 ? cap : 1;
+    w.mf = shared ? *shared : plan_mfma(A, wide, B, (long long)cap * 3 * dh, d);
     w.chunk = attn_chunk_for(f16, dh);
     w.nchunk_max = (n_cap + w.chunk - 1) / w.chunk;
-    w.fused = w.nchunk_max <= kFuseMaxChunks && B <= kMaxBatch;
+    w.fused = w.nchunk_max <= kFuseMaxChunks && !w.mf.on;
     w.q = A.take<float>((size_t)B * c * dh);
     w.part = A.take<float>((size_t)B * c * w.nchunk_max * (dh + 2));
     w.H = A.take<float>((size_t)B * c * dh);
-    const int nch = axpy_chunks(cap * dh, d, f16, w.fused ? dh : 0, &w.rpc);
+    // room for the chunks of every form the threshold may pick (vector ALU fused or not,
+    // matrix cores); the rows per chunk of the form in use
+    const bool can_fuse = w.nchunk_max <= kFuseMaxChunks;
+    int nch = axpy_chunks(cap * dh, d, f16, w.fused ? dh : 0, &w.rpc);
+    if (w.mf.reserved) {
+        int rpc_v = 0, rpc_m = 0;
+        nch = std::max(nch, axpy_chunks(cap * dh, d, f16, can_fuse ? dh : 0, &rpc_v));
+        nch = std::max(nch, axpy_chunks_mfma(cap * dh, d, &rpc_m));
+        if (w.mf.on) w.rpc = rpc_m;
+    }
     w.partial = A.take<float>((size_t)nch * B * d);
-    w.mf = plan_mfma(A, B, d, mfma_floats(B, (long long)cap * 3 * dh));
     return w;
 }
 
@@ -243,18 +270,19 @@ LayerWs plan_layer(Arena& A, const djv_model& m, bool dense) {
         w.idxM[i] = A.take<int32_t>(m.N);
         w.cntM[i] = A.take<int32_t>(1);
     }
-    w.mha = plan_mha(A, m.B, m.d, m.dh, capA, m.n_cap, f16);
-    w.mlp = plan_mlp(A, m.B, m.d, capM, f16);
-    if (!dense) {
-        w.predA = plan_predict(A, m.B, m.d, m.r, m.h, true);
-        w.predM = plan_predict(A, m.B, m.d, m.r, m.N, true);
-    } else {
-        w.predA = w.predM = PredWs{nullptr, nullptr, nullptr, MfmaWs{nullptr, nullptr}};
-    }
-    // the layer's largest launches: Q/K/V with both P1, both P2, MLP up
+    // one matrix-core scratch for every launch of the layer; its largest launches: Q/K/V
+    // with both P1, both P2, MLP up
     const long long rows = std::max({(long long)capA * 3 * m.dh + 2LL * m.r, (long long)m.h + m.N,
                                      (long long)capM});
-    w.mf = plan_mfma(A, m.B, std::max(m.d, m.r), mfma_floats(m.B, rows));
+    w.mf = plan_mfma(A, layer_wide(m), m.B, rows, std::max(m.d, m.r));
+    w.mha = plan_mha(A, m.B, m.d, m.dh, capA, m.n_cap, f16, true, &w.mf);
+    w.mlp = plan_mlp(A, m.B, m.d, capM, f16, true, &w.mf);
+    if (!dense) {
+        w.predA = plan_predict(A, m.B, m.d, m.r, m.h, true, true, &w.mf);
+        w.predM = plan_predict(A, m.B, m.d, m.r, m.N, true, true, &w.mf);
+    } else {
+        w.predA = w.predM = PredWs{nullptr, nullptr, nullptr, w.mf};
+    }
     return w;
 }
 
@@ -315,7 +343,7 @@ GemvSeg seg_up(const void* W1, const void* b1, const UnitList& neurons, const Ro
 GemvArgs gemv_args(int cols, int B, int prof, const MfmaWs& mf) {
     GemvArgs g{};
     g.cols = cols; g.B = B; g.flags = device_flags(); g.prof = prof;
-    g.yh = mf.yh; g.mfma_part = mf.part;
+    g.mfma = mf.on; g.mfma_part = mf.part;
     return g;
 }
 void add_seg(GemvArgs& g, const GemvSeg& S) { g.seg[g.nseg++] = S; }
@@ -344,7 +372,7 @@ djv_status run_down(bool f16, int B, int d, const void* W2, const UnitList& neur
     AxpyArgs x{};
     x.W = W2; x.cols = d; x.list = neurons; x.rpu = 1; x.coef = w.a; x.ldc = neurons.cap; x.B = B;
     x.partial = w.partial; x.rows_per_chunk = w.rpc; x.resid = resid;
-    x.out = out; x.stats = stats; x.flags = device_flags(); x.prof = DJV_PROF_MLP_DOWN;
+    x.out = out; x.stats = stats; x.mfma = w.mf.on; x.flags = device_flags(); x.prof = DJV_PROF_MLP_DOWN;
     DJV_HIP(launch_axpy(f16, x, s));
     return DJV_OK;
 }
@@ -388,7 +416,7 @@ djv_status run_oproj(bool f16, int B, int d, int dh, int n, const void* Wo, cons
     AxpyArgs x{};
     x.W = Wo; x.cols = d; x.list = heads; x.rpu = dh; x.coef = w.H; x.ldc = heads.cap * dh; x.B = B;
     x.partial = w.partial; x.rows_per_chunk = w.rpc; x.resid = resid; x.out = out; x.stats = stats;
-    x.flags = device_flags(); x.prof = DJV_PROF_O_PROJ;
+    x.mfma = w.mf.on; x.flags = device_flags(); x.prof = DJV_PROF_O_PROJ;
     if (w.fused) {
         x.attn_part = w.part;
         x.attn_nchunk = (n + 1 + w.chunk - 1) / w.chunk;
@@ -576,17 +604,17 @@ djv_status dejavu_workspace_bytes(int B, int d, int N, int h, int dh, int r, int
         const int n_out = N > h ? N : h;
         if (n_out > 0) {
             Arena a(nullptr);
-            plan_predict(a, Bq, d, r, n_out, true);
+            plan_predict(a, Bq, d, r, n_out, true, f16 && d % 32 == 0 && r % 32 == 0);
             upd(a.off);
         }
         if (N > 0 && d > 0) {
             Arena a(nullptr);
-            plan_mlp(a, Bq, d, N, f16);
+            plan_mlp(a, Bq, d, N, f16, f16 && d % 32 == 0);
             upd(a.off);
         }
         if (h > 0 && d > 0 && dh > 0) {
             Arena a(nullptr);
-            plan_mha(a, Bq, d, dh, h, n_cap > 0 ? n_cap : 1, f16);
+            plan_mha(a, Bq, d, dh, h, n_cap > 0 ? n_cap : 1, f16, f16 && d % 32 == 0);
             upd(a.off);
         }
         if (N > 0 && h > 0 && d > 0 && dh > 0) {
@@ -651,10 +679,11 @@ djv_status dejavu_predict(djv_dtype wt, int B, int d, int r, int n_out, const fl
     DJV_TRY(check_idx_ptr(count, "count"));
     DJV_TRY(check_opt_ptr(logits, "logits"));
     Arena sz(nullptr);
-    plan_predict(sz, B, d, r, n_out, logits == nullptr);
+    const bool wide = wide_possible(wt, {d, r});
+    plan_predict(sz, B, d, r, n_out, logits == nullptr, wide);
     DJV_TRY(check_ws(ws, ws_bytes, sz.off));
     Arena A(ws);
-    const PredWs w = plan_predict(A, B, d, r, n_out, logits == nullptr);
+    const PredWs w = plan_predict(A, B, d, r, n_out, logits == nullptr, wide);
     const PredJob j{P1, P2, n_out, (int)mode, k, t, idx, count, logits ? logits : w.z, &w};
     return run_predict(wt == DJV_F16, B, d, r, plain_input(y), &j, 1, w.mf, (hipStream_t)stream);
 }
@@ -677,10 +706,11 @@ static djv_status mlp_common(djv_dtype wt, int B, int d, int N, const float* y, 
     DJV_TRY(check_ptr(out, "out"));
     const bool f16 = wt == DJV_F16;
     Arena sz(nullptr);
-    plan_mlp(sz, B, d, cap, f16);
+    const bool wide = wide_possible(wt, {d});
+    plan_mlp(sz, B, d, cap, f16, wide);
     DJV_TRY(check_ws(ws, ws_bytes, sz.off));
     Arena A(ws);
-    const MlpWs w = plan_mlp(A, B, d, cap, f16);
+    const MlpWs w = plan_mlp(A, B, d, cap, f16, wide);
     return run_mlp(f16, B, d, N, plain_input(y), W1, b1, W2, idx, count, cap, resid, out, nullptr,
                    w, (hipStream_t)stream);
 }
@@ -726,10 +756,11 @@ static djv_status mha_common(djv_dtype wt, int B, int d, int h, int dh, int n, i
     DJV_TRY(check_ptr(out, "out"));
     const bool f16 = wt == DJV_F16;
     Arena sz(nullptr);
-    plan_mha(sz, B, d, dh, cap, n_cap, f16);
+    const bool wide = wide_possible(wt, {d});
+    plan_mha(sz, B, d, dh, cap, n_cap, f16, wide);
     DJV_TRY(check_ws(ws, ws_bytes, sz.off));
     Arena A(ws);
-    const MhaWs w = plan_mha(A, B, d, dh, cap, n_cap, f16);
+    const MhaWs w = plan_mha(A, B, d, dh, cap, n_cap, f16, wide);
     return run_mha(f16, B, d, h, dh, n, n_cap, plain_input(y), Wqkv, Wo, Kc, Vc, idx, count, cap,
                    scale, resid, out, nullptr, w, (hipStream_t)stream);
 }
@@ -882,6 +913,13 @@ djv_status dejavu_stack_decode(const djv_model* m, const djv_layer* layers, int 
         DJV_HIP(launch_gemv(f16, g, sm));
         DJV_TRY(run_down(f16, m->B, m->d, Ly.W2, neurons, w.xm, io.x_out, io.s_out, w.mlp, sm));
     }
+    return DJV_OK;
+}
+
+djv_status dejavu_set_mfma_min_batch(int b, int* previous) {
+    DJV_REQUIRE(b >= 1 && b <= kMaxBatch + 1, DJV_EINVAL, "b = %d outside [1, %d]", b, kMaxBatch + 1);
+    const int old = g_mfma_min_batch.exchange(b);
+    if (previous) *previous = old;
     return DJV_OK;
 }
 

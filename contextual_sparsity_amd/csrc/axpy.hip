@@ -254,38 +254,46 @@ __global__ __launch_bounds__(kFinGroups * kFinQuads) void axpy_finalize_kernel(A
 }
 
 // ---------------------------------------------------------------------------------
-// Batches of more than kMaxBatch rows (fp16 weights): the same partial tiles, computed on
-// the matrix cores.  D[b, c] = sum_r coef[b, r] W[r, c] over the block's rows is
-// v_mfma_f32_16x16x32_f16 with A = coefficients (rounded to fp16) and B = weights.  The
-// instruction wants 8 consecutive k (here: rows) per lane for one column, so each 32-row x
-// 64-column weight tile is staged through LDS: coalesced 16-byte row loads in, 16-bit
-// column reads out.  A block owns 64 columns (4 waves x 16) and a chunk of rows; the tiles
-// of a chunk are loaded kPrefetch at a time, one 16-byte load per thread per tile.
+// Matrix-core form (fp16 weights; batches of more than kMaxBatch rows, or smaller ones on
+// request): the same partial tiles, computed on the matrix cores.  D[b, c] = sum_r
+// coef[b, r] W[r, c] over the block's rows is v_mfma_f32_16x16x32_f16 with A =
+// coefficients (rounded to fp16) and B = weights.  The instruction wants 8 consecutive k
+// (here: rows) per lane for one column, while a weight row is contiguous in columns, so
+// the weights go through LDS: coalesced 16-byte row loads in, 16-bit column reads out.
+//
+// A block (4 waves) owns kAxCols = 256 columns, 64 per wave (4 column tiles of 16), and a
+// chunk of rows taken kAxGroup = 64 at a time: the group's weight tile (32 KiB) and its
+// coefficients sit in LDS while the next group's loads are already in registers.  One
+// coefficient fragment feeds the wave's four column tiles; one weight fragment feeds the
+// BT batch tiles.
 // ---------------------------------------------------------------------------------
 typedef _Float16 h8m_t __attribute__((ext_vector_type(8)));
 typedef float f4m_t __attribute__((ext_vector_type(4)));
-constexpr int kMfmaCols = 64;
-constexpr int kMfmaRows = 32;
-constexpr int kPrefetch = 8;
-constexpr int kWtPitch = kMfmaCols + 8;  // halfs per LDS row (padding against bank conflicts)
+constexpr int kAxCols = 256;                  // columns per block
+constexpr int kAxK = 32;                      // rows per MFMA
+constexpr int kAxGroup = 2 * kAxK;            // rows staged per round
+constexpr int kAxPitch = kAxCols + 4;         // halfs per LDS weight row (8-byte aligned rows)
+constexpr int kAxCfPitch = kAxGroup + 8;      // halfs per LDS coefficient row
+constexpr int kAxLoads = kAxGroup * kAxCols * 2 / 16 / kThreads;  // 16-byte loads per thread per round
+constexpr int kAxTargetBlocks = 1024;         // about four per compute unit (a constant, so that
+                                              // workspace sizes do not depend on the device)
 
 static __device__ const Vec16 g_zero16 = {};
 
 template <int BT>
 __global__ __launch_bounds__(kThreads) void axpy_mfma_kernel(AxpyArgs a) {
-    extern __shared__ float dyn[];  // [rpc] rows, then [BT * 16][rpc] fp16 coefficients
-    __shared__ _Float16 wt[kPrefetch][kMfmaRows][kWtPitch];
     constexpr int BP = BT * 16;
+    __shared__ _Float16 wt[kAxGroup][kAxPitch];
+    __shared__ _Float16 cf[BP][kAxCfPitch];
+    extern __shared__ int row_s[];  // [rows_per_chunk] weight row of each chunk row (-1: none)
     const int tid = threadIdx.x, wv = tid / kWave, l = tid % kWave;
     const int chunk = blockIdx.y;
-    const int c0 = blockIdx.x * kMfmaCols;
+    const int c0 = blockIdx.x * kAxCols;
     const int count = read_count(a.list, a.flags);
     const int rows = count * a.rpu;
     const int r0 = chunk * a.rows_per_chunk;
     if (r0 >= rows) return;
     const int nr = min(rows, r0 + a.rows_per_chunk) - r0;
-    int* row_s = reinterpret_cast<int*>(dyn);
-    _Float16* cf_s = reinterpret_cast<_Float16*>(dyn + a.rows_per_chunk);
     for (int i = tid; i < a.rows_per_chunk; i += kThreads) {
         int row = -1;
         if (i < nr) {
@@ -295,92 +303,106 @@ __global__ __launch_bounds__(kThreads) void axpy_mfma_kernel(AxpyArgs a) {
             row = unit < 0 ? -1 : unit * a.rpu + sub;
         }
         row_s[i] = row;
-        for (int b = 0; b < BP; ++b)
-            cf_s[b * a.rows_per_chunk + i] =
-                (_Float16)((row >= 0 && b < a.B) ? a.coef[(size_t)b * a.ldc + r0 + i] : 0.f);
     }
     __syncthreads();
 
-    // loads: thread t moves row t / 8, columns 8 (t % 8) .. + 8 of a tile
-    const int lr = tid / 8, lc = 8 * (tid % 8);
+    // weight loads: thread t moves columns 8 (t % 32) .. + 8 of rows t / 32 + 8 q
+    const int lc = 8 * (tid % 32), lr = tid / 32;
     const bool col_ok = c0 + lc + 8 <= a.cols;
     const char* Wb = reinterpret_cast<const char*>(a.W);
     const size_t row_bytes = (size_t)a.cols * 2;
-    auto load_tile = [&](int t) -> Vec16 {
-        const int i = t * kMfmaRows + lr;
-        const int row = i < nr ? row_s[i] : -1;
-        const char* p = (row >= 0 && col_ok) ? Wb + (size_t)row * row_bytes + (size_t)(c0 + lc) * 2
-                                             : reinterpret_cast<const char*>(&g_zero16);
-        return ldg16_nt(p);
+    // coefficient loads: thread t moves batch row t / 8, group rows 8 (t % 8) .. + 8
+    const int cb = tid / 8, cr = 8 * (tid % 8);
+    const int ngroups = (nr + kAxGroup - 1) / kAxGroup;
+
+    Vec16 wreg[kAxLoads];
+    float creg[8];
+    auto load_group = [&](int g) {
+#pragma unroll
+        for (int q = 0; q < kAxLoads; ++q) {
+            const int i = g * kAxGroup + lr + 8 * q;
+            const int row = i < nr ? row_s[i] : -1;
+            const char* p = (row >= 0 && col_ok) ? Wb + (size_t)row * row_bytes + (size_t)(c0 + lc) * 2
+                                                 : reinterpret_cast<const char*>(&g_zero16);
+            // a global (not flat) load: flat loads also count on lgkmcnt, so every LDS wait
+            // below would wait for them too
+            wreg[q] = ldg16_nt_at(reinterpret_cast<gchar*>(reinterpret_cast<uint64_t>(p)), 0);
+        }
+        if (cb < BP) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int i = g * kAxGroup + cr + e;
+                creg[e] = (cb < a.B && i < nr && row_s[i] >= 0) ? a.coef[(size_t)cb * a.ldc + r0 + i] : 0.f;
+            }
+        }
     };
-    const int ntiles = (nr + kMfmaRows - 1) / kMfmaRows;
-    f4m_t acc[BT];
+
+    f4m_t acc[4][BT];
 #pragma unroll
-    for (int t = 0; t < BT; ++t) acc[t] = f4m_t{0.f, 0.f, 0.f, 0.f};
-    const int col = wv * 16 + l % 16, kb = 8 * (l / 16);
-    Vec16 cur[kPrefetch];
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int q = 0; q < kPrefetch; ++q) cur[q] = load_tile(min(q, ntiles - 1));
-    for (int t0 = 0; t0 < ntiles; t0 += kPrefetch) {
+        for (int t = 0; t < BT; ++t) acc[j][t] = f4m_t{0.f, 0.f, 0.f, 0.f};
+    const int kb = 8 * (l / 16), cl = wv * 64 + l % 16;
+
+    load_group(0);
+    for (int g = 0; g < ngroups; ++g) {
 #pragma unroll
-        for (int q = 0; q < kPrefetch; ++q) *reinterpret_cast<Vec16*>(&wt[q][lr][lc]) = cur[q];
+        for (int q = 0; q < kAxLoads; ++q) {
+            // two 8-byte stores: rows are 8-byte aligned in LDS
+            uint2* dst = reinterpret_cast<uint2*>(&wt[lr + 8 * q][lc]);
+            dst[0] = make_uint2(wreg[q].w[0], wreg[q].w[1]);
+            dst[1] = make_uint2(wreg[q].w[2], wreg[q].w[3]);
+        }
+        if (cb < BP) {
+            h8m_t hv;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) hv[e] = (_Float16)creg[e];
+            *reinterpret_cast<h8m_t*>(&cf[cb][cr]) = hv;
+        }
         __syncthreads();
-        // the next tiles' loads go out before this group's products
+        if (g + 1 < ngroups) load_group(g + 1);
 #pragma unroll
-        for (int q = 0; q < kPrefetch; ++q) cur[q] = load_tile(min(t0 + kPrefetch + q, ntiles - 1));
+        for (int s = 0; s < kAxGroup / kAxK; ++s) {
+            h8m_t av[BT];
 #pragma unroll
-        for (int q = 0; q < kPrefetch; ++q) {
-            if (t0 + q >= ntiles) break;
-            h8m_t bw;
+            for (int t = 0; t < BT; ++t) av[t] = *reinterpret_cast<const h8m_t*>(&cf[16 * t + l % 16][s * kAxK + kb]);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) bw[e] = wt[q][kb + e][col];
-            const int rbase = (t0 + q) * kMfmaRows + kb;
+            for (int j = 0; j < 4; ++j) {
+                h8m_t bw;
 #pragma unroll
-            for (int t = 0; t < BT; ++t) {
-                const _Float16* cp = cf_s + (16 * t + l % 16) * a.rows_per_chunk + rbase;
-                h8m_t av;
+                for (int e = 0; e < 8; ++e) bw[e] = wt[s * kAxK + kb + e][cl + 16 * j];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) av[e] = rbase + e < a.rows_per_chunk ? cp[e] : (_Float16)0.f;
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bw, acc[t], 0, 0, 0);
+                for (int t = 0; t < BT; ++t) acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[t], bw, acc[j][t], 0, 0, 0);
             }
         }
         __syncthreads();
     }
-    // lane l holds D[b = 16 t + 4 (l / 16) + q][column wv * 16 + l % 16]
-    const int c = c0 + col;
-    if (c < a.cols) {
+    // lane l holds D[b = 16 t + 4 (l / 16) + q][column c0 + wv * 64 + 16 j + l % 16]
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int c = c0 + cl + 16 * j;
+        if (c >= a.cols) continue;
 #pragma unroll
         for (int t = 0; t < BT; ++t)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int b = 16 * t + 4 * (l / 16) + q;
-                if (b < a.B) a.partial[((size_t)chunk * a.B + b) * a.cols + c] = acc[t][q];
+                if (b < a.B) a.partial[((size_t)chunk * a.B + b) * a.cols + c] = acc[j][t][q];
             }
     }
 }
 
 template <typename T>
 hipError_t dispatch_mfma(const AxpyArgs& a, hipStream_t s) {
-    if (a.B > 32 || a.attn_part) return hipErrorInvalidValue;
+    if (a.B < 1 || a.B > kMaxBatchMfma || a.attn_part || a.rows_per_chunk % kAxGroup != 0)
+        return hipErrorInvalidValue;
     const int rows_cap = a.list.cap * a.rpu;
     const int nch = rows_cap > 0 ? (rows_cap + a.rows_per_chunk - 1) / a.rows_per_chunk : 0;
     if (nch > 0) {
-        const int bt = a.B <= 16 ? 1 : 2;
-        const size_t dyn = (size_t)a.rows_per_chunk * (bt * 16 * 2 + sizeof(int));
-        // chunks of up to kAxpyMaxChunkRows rows take more than 64 KiB of LDS in all
-        static const hipError_t opt_in = [] {
-            const int most = 160 * 1024 - (int)sizeof(_Float16) * kPrefetch * kMfmaRows * kWtPitch;
-            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&axpy_mfma_kernel<1>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, most);
-            if (e == hipSuccess)
-                e = hipFuncSetAttribute(reinterpret_cast<const void*>(&axpy_mfma_kernel<2>),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, most);
-            return e;
-        }();
-        if (opt_in != hipSuccess) return opt_in;
-        dim3 grid((a.cols + kMfmaCols - 1) / kMfmaCols, nch);
+        const size_t dyn = (size_t)a.rows_per_chunk * sizeof(int);
+        dim3 grid((a.cols + kAxCols - 1) / kAxCols, nch);
         prof_begin(a.prof, s);
-        if (bt == 1) hipLaunchKernelGGL(axpy_mfma_kernel<1>, grid, dim3(kThreads), dyn, s, a);
+        if (a.B <= 16) hipLaunchKernelGGL(axpy_mfma_kernel<1>, grid, dim3(kThreads), dyn, s, a);
         else hipLaunchKernelGGL(axpy_mfma_kernel<2>, grid, dim3(kThreads), dyn, s, a);
         prof_end(a.prof, s);
         hipError_t e = hipGetLastError();
@@ -393,10 +415,11 @@ hipError_t dispatch_mfma(const AxpyArgs& a, hipStream_t s) {
 
 template <typename T>
 hipError_t dispatch(const AxpyArgs& a, hipStream_t s) {
-    if (a.B > kMaxBatch) {
+    if (a.mfma) {
         if constexpr (sizeof(T) == 2) return dispatch_mfma<T>(a, s);
         else return hipErrorInvalidValue;
     }
+    if (a.B > kMaxBatch) return hipErrorInvalidValue;
     constexpr int E = WTraits<T>::kPerVec;
     const int tiles = (a.cols / E + kWave - 1) / kWave;
     const int rows_cap = a.list.cap * a.rpu;
@@ -425,10 +448,31 @@ hipError_t dispatch(const AxpyArgs& a, hipStream_t s) {
 
 }  // namespace
 
+int axpy_chunks_mfma(int rows_cap, int cols, int* rows_per_chunk) {
+    // about kAxTargetBlocks blocks over the column tiles and row chunks; chunks are whole
+    // staging rounds of kAxGroup rows, at most kAxpyMaxChunkRows
+    const int tiles = (cols + kAxCols - 1) / kAxCols;
+    const int step = kAxGroup;
+    if (rows_cap <= 0) {
+        *rows_per_chunk = step;
+        return 0;
+    }
+    int chunks = (kAxTargetBlocks + tiles - 1) / tiles;
+    const int max_chunks = (rows_cap + step - 1) / step;
+    if (chunks > max_chunks) chunks = max_chunks;
+    const int min_chunks = (rows_cap + kAxpyMaxChunkRows - 1) / kAxpyMaxChunkRows;
+    if (chunks < min_chunks) chunks = min_chunks;
+    if (chunks < 1) chunks = 1;
+    int rpc = (rows_cap + chunks - 1) / chunks;
+    rpc = ((rpc + step - 1) / step) * step;
+    if (rpc > kAxpyMaxChunkRows) rpc = kAxpyMaxChunkRows;
+    *rows_per_chunk = rpc;
+    return (rows_cap + rpc - 1) / rpc;
+}
+
 int axpy_chunks(int rows_cap, int cols, bool f16, int max_rows_per_chunk, int* rows_per_chunk) {
     const int E = f16 ? 8 : 4;
-    const int tiles = (cols / E + kWave - 1) / kWave;  // 512-column tiles (the matrix-core
-                                                       // form uses 64-column tiles, 8 per tile)
+    const int tiles = (cols / E + kWave - 1) / kWave;  // 512-column tiles
     const int step = kWavesPerBlock * kUnroll;  // 32 rows: one pass of the block
     if (rows_cap <= 0) {
         *rows_per_chunk = step;

@@ -291,19 +291,20 @@ struct GemvArgs {
     // selections and the GEMV segments; independent of both
     AttnArgs attn;
     int nattn;
-    // batches above kMaxBatch (matrix-core form): fp16 activation copies [seg][32, cols]
-    // and the k-slice partials (workspace, sized by mfma_shape)
-    __half* yh;
+    // matrix-core form (fp16 weights, cols % 32 == 0; required above kMaxBatch rows) and
+    // its k-slice partials (workspace, mfma_partial_floats)
+    bool mfma;
     float* mfma_part;
     unsigned* flags;
     int prof;             // profiling family of this launch (0: none)
 };
 
 hipError_t launch_gemv(bool f16, const GemvArgs& a, hipStream_t s);
-// Matrix-core form for B > kMaxBatch (fp16 weights, cols % 32 == 0): k-slices and the
-// partial floats a launch needs.
-void mfma_shape(const GemvArgs& a, int* slices, long long* floats);
-hipError_t launch_gemv_mfma(const GemvArgs& a, __half* Yh, float* partial, hipStream_t s);
+// Matrix-core form (fp16 weights, cols % 32 == 0, any B up to kMaxBatchMfma).  Partial
+// floats of any launch with rows_cap summed over its segments <= max_rows and
+// cols <= max_cols.
+long long mfma_partial_floats(int B, long long max_rows, int max_cols);
+hipError_t launch_gemv_mfma(const GemvArgs& a, float* partial, hipStream_t s);
 
 struct AxpyArgs {
     const void* W;        // [units*rpu, cols] weights
@@ -323,6 +324,7 @@ struct AxpyArgs {
     // needs rows_per_chunk <= rpu and nchunk <= kFuseMaxChunks); coef is then unused
     const float* attn_part;
     int attn_nchunk;
+    bool mfma;            // matrix-core form (fp16 weights; required above kMaxBatch rows)
     unsigned* flags;
     int prof;
 };
@@ -330,6 +332,8 @@ struct AxpyArgs {
 hipError_t launch_axpy(bool f16, const AxpyArgs& a, hipStream_t s);
 // Chunks of rows for a row-axpy over rows_cap rows (max_rows_per_chunk: 0 = no limit).
 int axpy_chunks(int rows_cap, int cols, bool f16, int max_rows_per_chunk, int* rows_per_chunk);
+// The same for the matrix-core form (fp16; chunks are multiples of 64 rows).
+int axpy_chunks_mfma(int rows_cap, int cols, int* rows_per_chunk);
 constexpr int kAxpyMaxChunkRows = 1024;
 
 // Partial (split-position) attention; with merge, also the merge kernel that writes H.

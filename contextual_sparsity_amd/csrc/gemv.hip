@@ -14,17 +14,18 @@ hipError_t launch_gemv(bool f16, const GemvArgs& a, hipStream_t s) {
         return hipErrorInvalidValue;
     for (int i = 0; i < a.nseg; ++i)
         if (a.seg[i].epi < kEpiStore || a.seg[i].epi > kEpiQkv) return hipErrorInvalidValue;
-    if (a.B > kMaxBatch) {
+    if (a.mfma) {
         // matrix-core form: side selections run first, on their own (their inputs are ready
         // before the launch, so the results are the same).  Attention chunks are left to the
         // caller: their unmerged partials feed only the vector-ALU O-projection.
-        if (!f16 || !a.yh || !a.mfma_part || a.nattn > 0) return hipErrorInvalidValue;
+        if (!f16 || !a.mfma_part || a.nattn > 0) return hipErrorInvalidValue;
         if (a.nside > 0) {
             const hipError_t e = launch_select(a.side, a.nside, a.B, s, 0);
             if (e != hipSuccess) return e;
         }
-        return launch_gemv_mfma(a, a.yh, a.mfma_part, s);
+        return launch_gemv_mfma(a, a.mfma_part, s);
     }
+    if (a.B > kMaxBatch) return hipErrorInvalidValue;
     bool long_rows = false;
     for (int i = 0; i < a.nside; ++i) long_rows = long_rows || a.side[i].n_out > kShortRows;
     if (long_rows && (a.nattn > 0 || a.B > 1)) {

@@ -396,8 +396,10 @@ hipError_t launch_shape(GemvArgs a, hipStream_t s) {
     const int slots = blocks_per_cu<T, TS, NV, NB, G, MODE>() * device_cus() * kOversub;
     if (MODE != 1) a.nattn = 0;
     if (MODE == 0) a.nside = 0;
+    // the prefix blocks (attention chunks, selections) are short; when they fill most of
+    // the device the GEMV still gets half of it, its blocks starting as the prefix retires
     const int nprefix = a.nattn + a.nside;
-    const int avail = slots - nprefix > 1 ? slots - nprefix : 1;
+    const int avail = slots - nprefix > slots / 2 ? slots - nprefix : (slots / 2 > 1 ? slots / 2 : 1);
     int want[kMaxSeg] = {0, 0, 0}, total_want = 0;
     for (int i = 0; i < a.nseg; ++i) {
         const long long rows_cap = (long long)a.seg[i].list.cap * a.seg[i].rpu;

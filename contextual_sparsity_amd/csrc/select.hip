@@ -18,11 +18,17 @@ __global__ __launch_bounds__(kThreads) void select_rows_kernel(SelectJobs jobs, 
     finish_row(S, J, blockIdx.x, B, (J.n_out + 31) / 32);
 }
 
-// Rows of at most 1024 scores: one block per selection over all B rows.
+// Rows of at most 1024 scores: one block per selection over all B rows (small B), or one
+// block per row writing the row's bitmap for compact_kernel (larger B).
 __global__ __launch_bounds__(kThreads) void select_small_kernel(SelectJobs jobs, int B) {
     __shared__ SmallShared<kThreads> S;
     select_small_block<kThreads>(S, jobs.j[blockIdx.x], B);
 }
+__global__ __launch_bounds__(kThreads) void select_small_rows_kernel(SelectJobs jobs) {
+    __shared__ SmallShared<kThreads> S;
+    select_small_row_bits<kThreads>(S, jobs.j[blockIdx.y], blockIdx.x);
+}
+constexpr int kSmallRowsFrom = 4;  // batches from which the per-row form is used
 
 __global__ __launch_bounds__(kThreads) void compact_kernel(SelectJobs jobs, int B) {
     const SelectJob& J = jobs.j[blockIdx.x];
@@ -31,10 +37,20 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(SelectJobs jobs, int 
     __shared__ int wtot[kThreads / kWave];
     const int w0 = 2 * tid, w1 = 2 * tid + 1;
     uint32_t m0 = 0u, m1 = 0u;
-    for (int b = 0; b < B; ++b) {
-        const uint32_t* bits = J.bits + (size_t)b * words;
-        if (w0 < words) m0 |= bits[w0];
-        if (w1 < words) m1 |= bits[w1];
+    // rows in groups of 8, their loads issued together
+    for (int b0 = 0; b0 < B; b0 += 8) {
+        uint32_t v0[8], v1[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const uint32_t* bits = J.bits + (size_t)min(b0 + k, B - 1) * words;
+            v0[k] = w0 < words ? bits[w0] : 0u;
+            v1[k] = w1 < words ? bits[w1] : 0u;
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            m0 |= v0[k];
+            m1 |= v1[k];
+        }
     }
     const int total = compact_words(m0, m1, J.idx, wtot);
     if (tid == 0) *J.count = total;
@@ -50,10 +66,19 @@ hipError_t launch_select(const SelectJob* jobs, int njobs, int B, hipStream_t s,
         js.j[i] = jobs[i];
         small = small && jobs[i].n_out <= kThreads;
     }
-    if (small) {
+    if (small && B < kSmallRowsFrom) {
         prof_begin(prof, s);
         hipLaunchKernelGGL(select_small_kernel, dim3(njobs), dim3(kThreads), 0, s, js, B);
         prof_end(prof, s);
+        return hipGetLastError();
+    }
+    if (small) {
+        prof_begin(prof, s);
+        hipLaunchKernelGGL(select_small_rows_kernel, dim3(B, njobs), dim3(kThreads), 0, s, js);
+        prof_end(prof, s);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(compact_kernel, dim3(njobs), dim3(kThreads), 0, s, js, B);
         return hipGetLastError();
     }
     prof_begin(prof, s);

@@ -608,5 +608,31 @@ __device__ __forceinline__ void select_small_block(SmallShared<NT>& S, const Sel
     if (tid == 0) *J.count = total;
 }
 
+// Row b alone (n <= NT): the same rank test as select_small_block, written as the row's
+// bitmap words (lane 0 of each wave stores its wave's 64 bits) for a union pass.
+template <int NT>
+__device__ __forceinline__ void select_small_row_bits(SmallShared<NT>& S, const SelectJob& J, int b) {
+    const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+    const int n = J.n_out, words = (n + 31) / 32;
+    const uint32_t key = score_key(J.z[(size_t)b * n + min(tid, n - 1)]);
+    bool sel;
+    if (J.mode == 1) {
+        sel = tid < n && key > J.tau_key;
+    } else {
+        S.keys[tid] = tid < n ? key : 0u;
+        __syncthreads();
+        int rank = 0;
+        for (int j = 0; j < n; ++j) {
+            const uint32_t kj = S.keys[j];
+            rank += (kj > key || (kj == key && j < tid)) ? 1 : 0;
+        }
+        sel = tid < n && rank < J.k;
+    }
+    const unsigned long long m = __ballot(sel);
+    uint32_t* out = J.bits + (size_t)b * words;
+    if (lane == 0 && 2 * w < words) out[2 * w] = (uint32_t)m;
+    if (lane == 0 && 2 * w + 1 < words) out[2 * w + 1] = (uint32_t)(m >> 32);
+}
+
 }  // namespace sel
 }  // namespace djv

@@ -30,7 +30,8 @@ EXPORTS = [
     "dejavu_workspace_bytes", "dejavu_workspace_bytes_model", "dejavu_layernorm", "dejavu_select",
     "dejavu_predict", "dejavu_sparse_mlp", "dejavu_dense_mlp", "dejavu_sparse_mha",
     "dejavu_dense_mha", "dejavu_sparse_layer", "dejavu_stack_decode", "dejavu_poll_device_error",
-    "dejavu_profile_kernel", "dejavu_profile_count", "dejavu_last_error", "dejavu_version",
+    "dejavu_set_mfma_min_batch", "dejavu_profile_kernel", "dejavu_profile_count",
+    "dejavu_last_error", "dejavu_version",
 ]
 
 DJV_PROF = {"off": 0, "qkv": 1, "mlp_up": 2, "mlp_down": 3, "o_proj": 4, "attn": 5, "pred_1": 6,
@@ -91,6 +92,7 @@ def lib() -> ctypes.CDLL:
             "dejavu_stack_decode": [ctypes.POINTER(djv_model), ctypes.POINTER(djv_layer), _I, _P, _I,
                                     _I, ctypes.POINTER(djv_trace), _P, _SZ, _P],
             "dejavu_poll_device_error": [_P, ctypes.POINTER(ctypes.c_uint32)],
+            "dejavu_set_mfma_min_batch": [_I, ctypes.POINTER(_I)],
             "dejavu_profile_kernel": [_I, ctypes.POINTER(_P), _I],
             "dejavu_profile_count": [ctypes.POINTER(_I)],
         }
@@ -262,6 +264,13 @@ def dejavu_poll_device_error(stream=None) -> int:
     v = ctypes.c_uint32(0)
     _check(lib().dejavu_poll_device_error(_stream(stream), ctypes.byref(v)))
     return v.value
+
+
+def dejavu_set_mfma_min_batch(b: int) -> int:
+    """Smallest batch that runs on the matrix cores (see the header); returns the old value."""
+    prev = _I(0)
+    _check(lib().dejavu_set_mfma_min_batch(int(b), ctypes.byref(prev)))
+    return prev.value
 
 
 def dejavu_profile_kernel(family, events=None) -> None:

@@ -234,6 +234,20 @@ djv_status dejavu_workspace_bytes_model(const djv_model* m, size_t* bytes);
 djv_status dejavu_poll_device_error(void* stream, uint32_t* flags);
 
 /* --------------------------------------------------------------------------------------
+ * dejavu_set_mfma_min_batch -- kernel form by batch size.  Calls whose batch has at least
+ *   `b` rows run their GEMVs and row-axpys on the matrix cores where that form applies
+ *   (DJV_F16 weights and every GEMV row length a multiple of 32); other calls with
+ *   B <= DJV_MAX_VALU_BATCH use the vector-ALU kernels.  Batches above DJV_MAX_VALU_BATCH
+ *   always use the matrix cores.  Default DJV_MAX_VALU_BATCH + 1; b must lie in
+ *   [1, DJV_MAX_VALU_BATCH + 1] (DJV_EINVAL otherwise).  *previous (host, may be NULL)
+ *   receives the value replaced.  Process-wide; each call reads it once when it plans its
+ *   launches, so a change does not affect work already enqueued.  Workspace sizes do not
+ *   depend on it.  The matrix-core form rounds the normalised activations and the
+ *   row-axpy coefficients to fp16.
+ * ------------------------------------------------------------------------------------ */
+djv_status dejavu_set_mfma_min_batch(int b, int* previous);
+
+/* --------------------------------------------------------------------------------------
  * Benchmark hook.  dejavu_profile_kernel(family, events, capacity): from now on, every
  *   launch of the given kernel family records events[2i] just before and events[2i+1]
  *   just after the i-th such launch, on that launch's stream, for i < capacity (later

@@ -178,3 +178,17 @@ def test_layer_and_stack_argument_errors():
     with pytest.raises(dj.DejavuError):
         dj.lib().dejavu_poll_device_error(None, None) and None or dj._check(
             dj.lib().dejavu_poll_device_error(None, None))
+
+
+def test_mfma_min_batch_setting():
+    assert _status(dj.dejavu_set_mfma_min_batch, 0) == dj.DJV_EINVAL
+    assert _status(dj.dejavu_set_mfma_min_batch, dj.DJV_MAX_VALU_BATCH + 2) == dj.DJV_EINVAL
+    old = dj.dejavu_set_mfma_min_batch(1)
+    assert old == dj.DJV_MAX_VALU_BATCH + 1
+    try:
+        # workspace sizes do not depend on the setting
+        a = dj.dejavu_workspace_bytes(2, 1024, 3000, 8, 128, 128, 200)
+        dj.dejavu_set_mfma_min_batch(dj.DJV_MAX_VALU_BATCH + 1)
+        assert dj.dejavu_workspace_bytes(2, 1024, 3000, 8, 128, 128, 200) == a
+    finally:
+        assert dj.dejavu_set_mfma_min_batch(old) in (1, dj.DJV_MAX_VALU_BATCH + 1)

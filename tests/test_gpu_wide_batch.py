@@ -1,6 +1,7 @@
-"""Batches of 5 to 32 tokens (the matrix-core GEMV and row-axpy) against the oracle:
-predictor scores and sets, sparse MLP, sparse attention with the KV append, a serial
-layer and a lookahead stack.  fp16 weights; row lengths are multiples of 32 and include
+"""The matrix-core GEMV and row-axpy against the oracle: batches of 5 to 32 tokens, and
+batches of 1 to 4 with the form forced by dejavu_set_mfma_min_batch.  Predictor scores
+and sets, sparse MLP, sparse attention with the KV append, a serial layer and a
+lookahead stack.  fp16 weights; row lengths are multiples of 32 and include
 a 64-column tile cut in half (d = 1056), ragged 16-row tiles (N = 1500, k = 37) and
 k-slices shorter than one unrolled step (r = 160).
 
@@ -136,3 +137,41 @@ def test_threshold_layer_wide():
     x, tr = st.run(lookahead=False, single_layer=True)
     assert 0 < tr["counts"][0, 1] < s.N
     check_stack(st, host(x), tr, lookahead=False)
+
+
+# ---------------------------------------------------- matrix-core form at small batches
+@pytest.fixture
+def mfma_from_1():
+    old = dj.dejavu_set_mfma_min_batch(1)
+    yield
+    dj.dejavu_set_mfma_min_batch(old)
+
+
+@pytest.mark.parametrize("B", [1, 2, 4])
+def test_small_batch_matrix_core_blocks(B, mfma_from_1):
+    print(f"matrix-core blocks B={B}", flush=True)
+    test_predict_wide("w-ragged", B)
+    test_sparse_mlp_wide("w-ragged", B)
+    test_sparse_mha_wide("w-dh64", B)
+    # the form did switch: the matrix-core row-axpy rounds its coefficients to fp16, so
+    # its bits differ from the vector-ALU result (both within the tolerance above)
+    s, w, p, x = _setup("w-ragged", B)
+    y = torch.from_numpy(O.layernorm(host(x)).astype(np.float32)).to(DEV)
+    idx, cnt, cap = idx_tensor(_random_set(s.N, 75, 75))
+    outs = []
+    for b_min in (1, dj.DJV_MAX_VALU_BATCH + 1):
+        dj.dejavu_set_mfma_min_batch(b_min)
+        out = torch.empty(B, s.d, device=DEV)
+        dj.dejavu_sparse_mlp(wt_code(s), B, s.d, s.N, y, w["W1"], w["b1"], w["W2"], idx, cnt, cap,
+                             None, out, ws_for(s))
+        outs.append(host(out))
+    torch.cuda.synchronize()
+    dj.dejavu_set_mfma_min_batch(1)
+    assert not np.array_equal(outs[0], outs[1])
+    assert rel_l2(outs[0], outs[1]) < TOL[s.dtype]
+
+
+@pytest.mark.parametrize("B", [1, 3])
+def test_small_batch_matrix_core_stack(B, mfma_from_1):
+    print(f"matrix-core lookahead stack B={B}", flush=True)
+    test_stack_wide(B)

@@ -108,13 +108,36 @@ __global__ __launch_bounds__(kThreads) void axpy_partial_kernel(AxpyArgs a) {
     const int nvec = a.cols / E;
     const int v = blockIdx.x * kWave + ln;              // this lane's column vector
     const bool col_ok = v < nvec;
-    const int count = read_count(a.list, a.flags);
+    const int count = read_count_uniform(a.list, a.flags);
     const int rows = count * a.rpu;
     const int r0 = chunk * a.rows_per_chunk;
     if (r0 >= rows) return;
     const int nr = min(rows, r0 + a.rows_per_chunk) - r0;
     float* cf_s = dyn;
     int* row_s = reinterpret_cast<int*>(dyn + NB * a.rows_per_chunk);
+    const char* Wb = reinterpret_cast<const char*>(a.W);
+    const size_t row_bytes = (size_t)a.cols * sizeof(T);
+
+    // the wave's first kUnroll rows (uniform over the wave: scalar index loads) are
+    // requested before the coefficients are staged, so their latency overlaps the staging
+    // (and the attention merge)
+    Vec16 w0[kUnroll];
+    const int wvu = __builtin_amdgcn_readfirstlane(wv);
+#pragma unroll
+    for (int q = 0; q < kUnroll; ++q) {
+        const int i = wvu + q * kWavesPerBlock;
+        int row = -1;
+        if (i < nr) {
+            const int r = r0 + i;
+            const int u = r / a.rpu, sub = r - u * a.rpu;
+            const int unit = unit_of_uniform(a.list, u, a.flags);
+            row = unit < 0 ? -1 : unit * a.rpu + sub;
+        }
+        if (row >= 0 && col_ok)
+            w0[q] = ldg16_nt(Wb + (size_t)row * row_bytes + (size_t)v * 16);
+        else
+            w0[q] = Vec16{{0u, 0u, 0u, 0u}};
+    }
 
     if (a.attn_part) {
         float* wm = dyn + (NB + 1) * a.rows_per_chunk;
@@ -134,25 +157,12 @@ __global__ __launch_bounds__(kThreads) void axpy_partial_kernel(AxpyArgs a) {
     }
     __syncthreads();
 
-    const char* Wb = reinterpret_cast<const char*>(a.W);
-    const size_t row_bytes = (size_t)a.cols * sizeof(T);
     float acc[NB][E];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[b][e] = 0.f;
-
-    for (int i0 = wv; i0 < nr; i0 += kWavesPerBlock * kUnroll) {
-        Vec16 w[kUnroll];
-#pragma unroll
-        for (int q = 0; q < kUnroll; ++q) {
-            const int i = i0 + q * kWavesPerBlock;
-            const int row = i < nr ? row_s[i] : -1;
-            if (row >= 0 && col_ok)
-                w[q] = ldg16_nt(Wb + (size_t)row * row_bytes + (size_t)v * 16);
-            else
-                w[q] = Vec16{{0u, 0u, 0u, 0u}};
-        }
+    auto consume = [&](const Vec16 (&w)[kUnroll], int i0) {
 #pragma unroll
         for (int q = 0; q < kUnroll; ++q) {
             const int i = i0 + q * kWavesPerBlock;
@@ -166,6 +176,20 @@ __global__ __launch_bounds__(kThreads) void axpy_partial_kernel(AxpyArgs a) {
                 for (int e = 0; e < E; ++e) acc[b][e] = fmaf(c, f[e], acc[b][e]);
             }
         }
+    };
+    consume(w0, wv);
+    for (int i0 = wv + kWavesPerBlock * kUnroll; i0 < nr; i0 += kWavesPerBlock * kUnroll) {
+        Vec16 w[kUnroll];
+#pragma unroll
+        for (int q = 0; q < kUnroll; ++q) {
+            const int i = i0 + q * kWavesPerBlock;
+            const int row = i < nr ? row_s[i] : -1;
+            if (row >= 0 && col_ok)
+                w[q] = ldg16_nt(Wb + (size_t)row * row_bytes + (size_t)v * 16);
+            else
+                w[q] = Vec16{{0u, 0u, 0u, 0u}};
+        }
+        consume(w, i0);
     }
 
     if (wv > 0) {

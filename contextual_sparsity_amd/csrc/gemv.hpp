@@ -438,6 +438,22 @@ hipError_t dispatch_nv(const GemvArgs& a, int nv, hipStream_t s) {
         default:
             return hipErrorInvalidValue;
         }
+    } else if constexpr (MODE != 2 && NB == 1) {
+        // long rows at one batch row in 256-thread blocks: two rows per group, so a team
+        // has four rows in flight (the short launches of a layer are one or two latency
+        // rounds, not a stream)
+        switch (nv) {
+            DJV_GEMV_CASE(1, 2)
+            DJV_GEMV_CASE(2, 2)
+            DJV_GEMV_CASE(3, 2)
+            DJV_GEMV_CASE(4, 2)
+            DJV_GEMV_CASE(5, 2)
+            DJV_GEMV_CASE(6, 2)
+            DJV_GEMV_CASE(7, 2)
+            DJV_GEMV_CASE(8, 2)
+        default:
+            return hipErrorInvalidValue;
+        }
     } else {
         switch (nv) {
             DJV_GEMV_CASE(1, 2)

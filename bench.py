@@ -14,7 +14,9 @@ per layer, the dense path on the same stack, the roofline of the dominant kernel
 (head-sparse Q/K/V GEMV) measured with HIP events around its launches, and the CPU
 oracle timed on a bounded sample of the same workload.
 
---sweep instead times OPT-175B-shaped layers over neuron keep-percentages
+--ablation times the fused sparse MLP against gather-then-dense (the pages' kernel-fusion
+claim) at a few keep-percentages.  --sweep instead times OPT-175B-shaped layers over
+neuron keep-percentages
 {1..100}, head keep-percentages {10..100} and batches {1..32} (union index sets),
 with the vector-ALU and the matrix-core kernel forms where both apply and the dense path
 per batch, and prints one JSON line per point.
@@ -78,6 +80,8 @@ def parse(argv=None):
     ap.add_argument("--sweep-layers", type=int, default=8, help="distinct layers per sweep step")
     ap.add_argument("--sweep-steps", type=int, default=5)
     ap.add_argument("--sweep-batches", default="", help="comma list overriding the sweep's batches")
+    ap.add_argument("--ablation", action="store_true",
+                    help="the fusion ablation: fused sparse MLP vs gather-then-dense, OPT-175B shape")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 1 GiB three times (reference for HBM byte "
                          "counters) and exit")
@@ -144,6 +148,71 @@ def cpu_baseline(wl, s, layers_gpu, preds_gpu, x0, k_A, k_M, budget_s, lb):
         "sample": f"first {done} of {len(layers_gpu)} layers of one decode step (float64 numpy "
                   f"oracle, lookahead sets), {t_total:.1f} s of CPU work",
     }
+
+
+# ------------------------------------------------------------------------ fusion ablation
+def ablation(args) -> int:
+    """Fused gather-and-multiply (the library's sparse MLP, kept rows read in place) against
+    the unfused form: kept W1 rows, b1 entries and W2 rows gathered into contiguous copies,
+    then the dense MLP over the copies (three passes over the kept bytes instead of one)."""
+    import torch
+    from contextual_sparsity_amd import configs, synth
+    from contextual_sparsity_amd import dejavu as dj
+
+    base = configs.WORKLOADS["opt175b-1layer-fp16"]
+    s = base.shape
+    dev = "cuda"
+    w = synth.make_layer(s, args.seed, 0, dev)
+    x = synth.make_input(s, args.seed, dev)
+    y = torch.empty_like(x)
+    dj.dejavu_layernorm(1, s.d, x, y, 1e-5)
+    ws = dj.workspace(dj.dejavu_workspace_bytes(1, s.d, s.N, s.h, s.dh, s.r, s.cap), dev)
+    out = torch.empty_like(x)
+    e = 2
+    for pct in (1, 5, 10, 25):
+        k = configs.keep(pct, s.N)
+        g = torch.Generator(device="cpu").manual_seed(args.seed + pct)
+        S = torch.randperm(s.N, generator=g)[:k].sort().values.to(torch.int32).to(dev)
+        cnt = torch.tensor([k], dtype=torch.int32, device=dev)
+        W1g = torch.empty(k, s.d, dtype=torch.float16, device=dev)
+        W2g = torch.empty_like(W1g)
+        b1g = torch.empty(k, dtype=torch.float16, device=dev)
+
+        def fused():
+            dj.dejavu_sparse_mlp(dj.DJV_F16, 1, s.d, s.N, y, w["W1"], w["b1"], w["W2"], S, cnt, k, x, out, ws)
+
+        def unfused():
+            dj.dejavu_gather_rows(dj.DJV_F16, 1, s.d, s.N, w["W1"], S, cnt, k, W1g)
+            dj.dejavu_gather_rows(dj.DJV_F16, 1, 1, s.N, w["b1"], S, cnt, k, b1g)
+            dj.dejavu_gather_rows(dj.DJV_F16, 1, s.d, s.N, w["W2"], S, cnt, k, W2g)
+            dj.dejavu_dense_mlp(dj.DJV_F16, 1, s.d, k, y, W1g, b1g, W2g, x, out, ws)
+
+        def gather_only():
+            dj.dejavu_gather_rows(dj.DJV_F16, 1, s.d, s.N, w["W1"], S, cnt, k, W1g)
+            dj.dejavu_gather_rows(dj.DJV_F16, 1, 1, s.N, w["b1"], S, cnt, k, b1g)
+            dj.dejavu_gather_rows(dj.DJV_F16, 1, s.d, s.N, w["W2"], S, cnt, k, W2g)
+
+        def timed(f, n=30):
+            for _ in range(3):
+                f()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(n):
+                f()
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) * 1e3 / n
+
+        kept = 2 * k * s.d * e + k * e
+        t_f, t_u, t_g = timed(fused), timed(unfused), timed(gather_only)
+        pt = {"ablation": "fused gather-multiply vs gather then dense", "workload": "opt175b MLP, fp16, B 1",
+              "pct_M": pct, "k_M": k, "kept_bytes": kept,
+              "fused_us": round(t_f, 2), "fused_bytes": kept, "fused_GBps": round(kept / (t_f * 1e-6) / 1e9, 1),
+              "unfused_us": round(t_u, 2), "unfused_bytes": 3 * kept, "gather_us": round(t_g, 2),
+              "speedup_fused": round(t_u / t_f, 3)}
+        print(json.dumps(pt), flush=True)
+    return 0
 
 
 # ------------------------------------------------------------------------ sparsity x batch sweep
@@ -246,6 +315,8 @@ def main(argv=None) -> int:
         return 2
     if args.sweep:
         return sweep(args)
+    if args.ablation:
+        return ablation(args)
     import torch
     from contextual_sparsity_amd import configs, synth
     from contextual_sparsity_amd import dejavu as dj

@@ -19,6 +19,13 @@
 
 using namespace djv;
 
+namespace djv {
+// gather.hip: kept rows copied to a contiguous buffer (the unfused gather of the fusion
+// ablation); row_bytes a multiple of 2.
+hipError_t launch_gather_rows(const void* W, void* out, const UnitList& list, int rpu, size_t row_bytes,
+                              unsigned* flags, hipStream_t s);
+}  // namespace djv
+
 namespace {
 
 thread_local std::string g_err;
@@ -642,6 +649,25 @@ djv_status dejavu_layernorm(int B, int d, const float* x, float* y, float eps, v
     DJV_TRY(check_ptr(x, "x"));
     DJV_TRY(check_ptr(y, "y"));
     DJV_HIP(launch_layernorm(B, d, x, y, eps, (hipStream_t)stream));
+    return DJV_OK;
+}
+
+djv_status dejavu_gather_rows(djv_dtype wt, int rpu, int cols, int units, const void* W,
+                              const int32_t* idx, const int32_t* count, int cap, void* out,
+                              void* stream) {
+    DJV_TRY(check_dtype(wt));
+    DJV_REQUIRE(rpu >= 1 && cols >= 1 && units >= 1, DJV_EINVAL, "rpu, cols and units must be >= 1");
+    DJV_REQUIRE(cap >= 1 && cap <= units, DJV_EINVAL, "cap = %d outside [1, units = %d]", cap, units);
+    DJV_REQUIRE((long long)cap * rpu <= 0x7fffffffLL && (long long)units * rpu <= 0x7fffffffLL, DJV_EUNSUPPORTED,
+                "too many rows");
+    const size_t row_bytes = (size_t)cols * esize(wt);
+    const size_t al = row_bytes % 16 == 0 ? 16 : (row_bytes % 4 == 0 ? 4 : 2);
+    DJV_REQUIRE(W != nullptr && out != nullptr, DJV_EINVAL, "W and out must not be NULL");
+    DJV_REQUIRE(aligned(W, al) && aligned(out, al), DJV_EALIGN, "W and out must be %zu-byte aligned", al);
+    DJV_TRY(check_idx_ptr(idx, "idx"));
+    if (count) DJV_TRY(check_idx_ptr(count, "count"));
+    const UnitList list{idx, count, cap, units};
+    DJV_HIP(launch_gather_rows(W, out, list, rpu, row_bytes, device_flags(), (hipStream_t)stream));
     return DJV_OK;
 }
 

@@ -30,7 +30,7 @@ EXPORTS = [
     "dejavu_workspace_bytes", "dejavu_workspace_bytes_model", "dejavu_layernorm", "dejavu_select",
     "dejavu_predict", "dejavu_sparse_mlp", "dejavu_dense_mlp", "dejavu_sparse_mha",
     "dejavu_dense_mha", "dejavu_sparse_layer", "dejavu_stack_decode", "dejavu_poll_device_error",
-    "dejavu_set_mfma_min_batch", "dejavu_profile_kernel", "dejavu_profile_count",
+    "dejavu_set_mfma_min_batch", "dejavu_gather_rows", "dejavu_profile_kernel", "dejavu_profile_count",
     "dejavu_last_error", "dejavu_version",
 ]
 
@@ -93,6 +93,7 @@ def lib() -> ctypes.CDLL:
                                     _I, ctypes.POINTER(djv_trace), _P, _SZ, _P],
             "dejavu_poll_device_error": [_P, ctypes.POINTER(ctypes.c_uint32)],
             "dejavu_set_mfma_min_batch": [_I, ctypes.POINTER(_I)],
+            "dejavu_gather_rows": [_I, _I, _I, _I, _P, _P, _P, _I, _P, _P],
             "dejavu_profile_kernel": [_I, ctypes.POINTER(_P), _I],
             "dejavu_profile_count": [ctypes.POINTER(_I)],
         }
@@ -264,6 +265,12 @@ def dejavu_poll_device_error(stream=None) -> int:
     v = ctypes.c_uint32(0)
     _check(lib().dejavu_poll_device_error(_stream(stream), ctypes.byref(v)))
     return v.value
+
+
+def dejavu_gather_rows(wt, rpu, cols, units, W, idx, count, cap, out, stream=None) -> None:
+    """The unfused gather of the fusion ablation (see the header)."""
+    _check(lib().dejavu_gather_rows(int(wt), int(rpu), int(cols), int(units), _ptr(W), _ptr(idx),
+                                    _ptr(count), int(cap), _ptr(out), _stream(stream)))
 
 
 def dejavu_set_mfma_min_batch(b: int) -> int:

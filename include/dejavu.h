@@ -133,6 +133,22 @@ djv_status dejavu_sparse_mlp(djv_dtype wt, int B, int d, int N, const float* y,
                              const float* resid, float* out,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* --------------------------------------------------------------------------------------
+ * dejavu_gather_rows -- the unfused form of the gather, for the fusion ablation:
+ *   out[slot * rpu + j] = W[idx[slot] * rpu + j] for slot < count and 0 <= j < rpu, and
+ *   zero rows for count <= slot < cap (rows of `cols` elements of dtype wt).
+ *   [BLOG section 3.2 "Kernel Fusion"]: without fusion the kept rows are read, written to a
+ *   contiguous copy W' and read again by the product (three passes over the kept bytes);
+ *   the library's sparse calls never do this, they read the kept rows in place.
+ *   W: [units * rpu, cols], out: [cap * rpu, cols] (device; 16-byte aligned when a row is
+ *   a multiple of 16 bytes, 4-byte when a multiple of 4, else 2-byte).  idx / count as in
+ *   dejavu_sparse_mlp (count NULL: cap).  An index outside [0, units) gives a zero row and
+ *   sets DJV_FLAG_BAD_INDEX.  cols >= 1, rpu >= 1, 1 <= cap <= units.
+ * ------------------------------------------------------------------------------------ */
+djv_status dejavu_gather_rows(djv_dtype wt, int rpu, int cols, int units, const void* W,
+                              const int32_t* idx, const int32_t* count, int cap, void* out,
+                              void* stream);
+
 /* dejavu_dense_mlp -- the same with S = all N neurons (the dense comparison path). */
 djv_status dejavu_dense_mlp(djv_dtype wt, int B, int d, int N, const float* y,
                             const void* W1, const void* b1, const void* W2,

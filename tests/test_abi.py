@@ -192,3 +192,23 @@ def test_mfma_min_batch_setting():
         assert dj.dejavu_workspace_bytes(2, 1024, 3000, 8, 128, 128, 200) == a
     finally:
         assert dj.dejavu_set_mfma_min_batch(old) in (1, dj.DJV_MAX_VALU_BATCH + 1)
+
+
+def test_gather_rows_argument_errors():
+    g = dj.dejavu_gather_rows
+    ok = dict(wt=dj.DJV_F16, rpu=1, cols=768, units=3072, W=A, idx=A, count=A, cap=154, out=A)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return _status(g, **a)
+    assert call(wt=3) == dj.DJV_EINVAL
+    assert call(rpu=0) == dj.DJV_EINVAL
+    assert call(cols=0) == dj.DJV_EINVAL
+    assert call(cap=0) == dj.DJV_EINVAL
+    assert call(cap=3073) == dj.DJV_EINVAL
+    assert call(W=None) == dj.DJV_EINVAL
+    assert call(idx=None) == dj.DJV_EINVAL
+    assert call(count=A + 2) == dj.DJV_EALIGN
+    assert call(out=MIS) == dj.DJV_EALIGN          # 1536-byte rows need 16-byte alignment
+    assert call(cols=2, out=A + 2) == dj.DJV_EALIGN  # 4-byte rows need 4-byte alignment

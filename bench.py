@@ -80,6 +80,9 @@ def parse(argv=None):
     ap.add_argument("--sweep-layers", type=int, default=8, help="distinct layers per sweep step")
     ap.add_argument("--sweep-steps", type=int, default=5)
     ap.add_argument("--sweep-batches", default="", help="comma list overriding the sweep's batches")
+    ap.add_argument("--threshold", action="store_true",
+                    help="threshold-mode selection: t calibrated on layer 0's scores to the keep "
+                         "percentages; one JSON line with the kept-count spread")
     ap.add_argument("--ablation", action="store_true",
                     help="the fusion ablation: fused sparse MLP vs gather-then-dense, OPT-175B shape")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -353,6 +356,27 @@ def main(argv=None) -> int:
     x0 = synth.make_input(s, args.seed, dev)
     wt = dj.DJV_F16 if s.dtype == "f16" else dj.DJV_F32
     m = dj.make_model(wt, s.B, s.d, s.N, s.h, s.dh, s.r, s.n, s.cap, wl.scale, dj.DJV_TOPK, k_A, k_M)
+    thr = None
+    if args.threshold:
+        # t_A, t_M: sigmoid of the score quantiles that keep pct_A / pct_M of layer 0's units
+        # (calibrated once on the host from the library's own scores; the step then selects
+        # by threshold on the device, so the kept count varies per layer and token)
+        import torch.nn.functional as F
+        xn = torch.empty_like(x0)
+        dj.dejavu_layernorm(s.B, s.d, x0, xn, 1e-5)
+        ts = []
+        for P1, P2, n_out, pct in ((preds[0]["P1_A"], preds[0]["P2_A"], s.h, wl.pct_A),
+                                   (preds[0]["P1_M"], preds[0]["P2_M"], s.N, wl.pct_M)):
+            z = torch.empty(s.B, n_out, dtype=torch.float32, device=dev)
+            idx = torch.empty(n_out, dtype=torch.int32, device=dev)
+            cnt = torch.empty(1, dtype=torch.int32, device=dev)
+            pws = dj.workspace(dj.dejavu_workspace_bytes(s.B, s.d, s.N, s.h, s.dh, s.r, s.cap), dev)
+            dj.dejavu_predict(wt, s.B, s.d, s.r, n_out, xn, P1, P2, dj.DJV_TOPK, 1, 0.5, idx, cnt, z, pws)
+            q = torch.quantile(z.flatten().double().cpu(), 1.0 - pct / 100.0).item()
+            ts.append(float(torch.sigmoid(torch.tensor(q)).item()))
+        m = dj.make_model(wt, s.B, s.d, s.N, s.h, s.dh, s.r, s.n, s.cap, wl.scale, dj.DJV_THRESHOLD, 0, 0,
+                          t_A=ts[0], t_M=ts[1])
+        thr = {"t_A": ts[0], "t_M": ts[1]}
     desc = [dj.make_layer(layers[l], preds[l]) for l in range(L)]
     ws = dj.workspace(dj.dejavu_workspace_bytes_model(m), dev)
     x = x0.clone()
@@ -381,6 +405,27 @@ def main(argv=None) -> int:
     log("warm-up done")
     ms_step, wall_ms = timed(args.steps)
     log(f"sparse step {ms_step:.3f} ms (wall {wall_ms:.3f} ms)")
+    if thr is not None:
+        counts = torch.zeros(L, 2, dtype=torch.int32, device=dev)
+        x.copy_(x0)
+        dj.dejavu_stack_decode(m, desc, x, lookahead, False, dj.make_trace(counts=counts), ws, s_main)
+        c = counts.cpu().double()
+        e = 2 if s.dtype == "f16" else 4
+        lbs = [(2 * s.d * s.r + s.r * s.N + s.r * s.h) * e + 4 * s.d * s.dh * int(c[l, 0]) * e
+               + s.B * 2 * (s.n + 1) * s.dh * int(c[l, 0]) * e + (2 * s.d + 1) * int(c[l, 1]) * e for l in range(L)]
+        step_bytes_t = sum(lbs)
+        out = {"mode": "threshold", "workload": wl.name, "layers": L, "t_A": round(thr["t_A"], 6),
+               "t_M": round(thr["t_M"], 6), "ms_per_step": round(ms_step, 4),
+               "us_per_layer": round(ms_step * 1e3 / L, 2),
+               "GBps": round(step_bytes_t / (ms_step * 1e-3) / 1e9, 1),
+               "pct_of_peak": round(100 * step_bytes_t / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+               "kept_heads": {"mean": round(c[:, 0].mean().item(), 2), "min": int(c[:, 0].min()),
+                              "max": int(c[:, 0].max())},
+               "kept_neurons": {"mean": round(c[:, 1].mean().item(), 1), "min": int(c[:, 1].min()),
+                                "max": int(c[:, 1].max())},
+               "bytes_per_layer_mean": round(step_bytes_t / L)}
+        print(json.dumps(out), flush=True)
+        return 0
     lb = layer_bytes(s, k_A, k_M)
     step_bytes = lb["total"] * L
     gbs = step_bytes / (ms_step * 1e-3) / 1e9

@@ -27,6 +27,17 @@ constexpr int kUnroll = 8;      // rows in flight per wave
 constexpr int kWavesPerBlock = 4;
 constexpr int kThreads = 256;
 
+// Rows per chunk for the rows actually kept: the launch has one chunk per rows_per_chunk
+// rows of the capacity; when the device count is lower (a threshold list, a batch union)
+// the rows are spread over all of them in multiples of chunk_step, so every block has work.
+__device__ __forceinline__ int chunk_rows(const AxpyArgs& a, int rows) {
+    const int rows_cap = a.list.cap * a.rpu;
+    const int nch_cap = (rows_cap + a.rows_per_chunk - 1) / a.rows_per_chunk;
+    int r = (rows + nch_cap - 1) / nch_cap;
+    r = (r + a.chunk_step - 1) / a.chunk_step * a.chunk_step;
+    return min(max(r, a.chunk_step), a.rows_per_chunk);
+}
+
 // Coefficients of this chunk's rows merged from split-position attention partials: row
 // r = u * dh + c (unit slot u, dim c) of batch row b gets
 //   sum_ch e^{m_ch - M} acc_ch[c] / sum_ch e^{m_ch - M} l_ch,   M = max_ch m_ch,
@@ -110,9 +121,10 @@ __global__ __launch_bounds__(kThreads) void axpy_partial_kernel(AxpyArgs a) {
     const bool col_ok = v < nvec;
     const int count = read_count_uniform(a.list, a.flags);
     const int rows = count * a.rpu;
-    const int r0 = chunk * a.rows_per_chunk;
+    const int rpc = chunk_rows(a, rows);
+    const int r0 = chunk * rpc;
     if (r0 >= rows) return;
-    const int nr = min(rows, r0 + a.rows_per_chunk) - r0;
+    const int nr = min(rows, r0 + rpc) - r0;
     float* cf_s = dyn;
     int* row_s = reinterpret_cast<int*>(dyn + NB * a.rows_per_chunk);
     const char* Wb = reinterpret_cast<const char*>(a.W);
@@ -235,7 +247,8 @@ __global__ __launch_bounds__(kFinGroups * kFinQuads) void axpy_finalize_kernel(A
     const int ncols = min(kLnTile, a.cols - c0);
     const int count = read_count(a.list, nullptr);
     const int rows = count * a.rpu;
-    const int nch = (rows + a.rows_per_chunk - 1) / a.rows_per_chunk;
+    const int rpc = chunk_rows(a, rows);
+    const int nch = (rows + rpc - 1) / rpc;
     const size_t plane = (size_t)a.B * a.cols;
     // a whole float4 inside the row, or (ragged last slice) a clamped one whose sum is unused
     const bool q_ok = 4 * q + 4 <= ncols;
@@ -315,9 +328,10 @@ __global__ __launch_bounds__(kThreads) void axpy_mfma_kernel(AxpyArgs a) {
     const int c0 = blockIdx.x * kAxCols;
     const int count = read_count(a.list, a.flags);
     const int rows = count * a.rpu;
-    const int r0 = chunk * a.rows_per_chunk;
+    const int rpc = chunk_rows(a, rows);
+    const int r0 = chunk * rpc;
     if (r0 >= rows) return;
-    const int nr = min(rows, r0 + a.rows_per_chunk) - r0;
+    const int nr = min(rows, r0 + rpc) - r0;
     for (int i = tid; i < a.rows_per_chunk; i += kThreads) {
         int row = -1;
         if (i < nr) {
@@ -417,7 +431,9 @@ __global__ __launch_bounds__(kThreads) void axpy_mfma_kernel(AxpyArgs a) {
 }
 
 template <typename T>
-hipError_t dispatch_mfma(const AxpyArgs& a, hipStream_t s) {
+hipError_t dispatch_mfma(const AxpyArgs& args, hipStream_t s) {
+    AxpyArgs a = args;
+    a.chunk_step = kAxGroup;
     if (a.B < 1 || a.B > kMaxBatchMfma || a.attn_part || a.rows_per_chunk % kAxGroup != 0)
         return hipErrorInvalidValue;
     const int rows_cap = a.list.cap * a.rpu;
@@ -438,11 +454,13 @@ hipError_t dispatch_mfma(const AxpyArgs& a, hipStream_t s) {
 }
 
 template <typename T>
-hipError_t dispatch(const AxpyArgs& a, hipStream_t s) {
-    if (a.mfma) {
-        if constexpr (sizeof(T) == 2) return dispatch_mfma<T>(a, s);
+hipError_t dispatch(const AxpyArgs& args, hipStream_t s) {
+    if (args.mfma) {
+        if constexpr (sizeof(T) == 2) return dispatch_mfma<T>(args, s);
         else return hipErrorInvalidValue;
     }
+    AxpyArgs a = args;
+    a.chunk_step = kWavesPerBlock * kUnroll;
     if (a.B > kMaxBatch) return hipErrorInvalidValue;
     constexpr int E = WTraits<T>::kPerVec;
     const int tiles = (a.cols / E + kWave - 1) / kWave;

@@ -295,6 +295,9 @@ struct GemvArgs {
     // its k-slice partials (workspace, mfma_partial_floats)
     bool mfma;
     float* mfma_part;
+    // set by the launcher: the dynamic segment split of the vector-ALU GEMV (segments that
+    // read the same input, with device counts)
+    bool dyn;
     unsigned* flags;
     int prof;             // profiling family of this launch (0: none)
 };
@@ -315,7 +318,8 @@ struct AxpyArgs {
     int ldc;
     int B;
     float* partial;       // [nchunk, B, cols] workspace
-    int rows_per_chunk;
+    int rows_per_chunk;   // chunk size for the full capacity (LDS is sized for it); with
+                          // fewer rows kept the chunks shrink so every chunk has rows
     const float* resid;   // may be nullptr
     float* out;           // [B, cols]
     float2* stats;        // [B, ceil(cols / kLnTile)] (mean, M2) of each slice of out, or nullptr
@@ -325,6 +329,7 @@ struct AxpyArgs {
     const float* attn_part;
     int attn_nchunk;
     bool mfma;            // matrix-core form (fp16 weights; required above kMaxBatch rows)
+    int chunk_step;       // set by the launcher: chunks are multiples of this many rows
     unsigned* flags;
     int prof;
 };

@@ -8,6 +8,12 @@ hipError_t launch_gemv_f32(const GemvArgs& a, hipStream_t s);
 hipError_t launch_gemv_f32_side(const GemvArgs& a, hipStream_t s);
 hipError_t launch_gemv_f16(const GemvArgs& a, hipStream_t s);
 hipError_t launch_gemv_f16_side(const GemvArgs& a, hipStream_t s);
+hipError_t launch_gemv_f32_dyn(const GemvArgs& a, hipStream_t s);
+hipError_t launch_gemv_f32_side_dyn(const GemvArgs& a, hipStream_t s);
+hipError_t launch_gemv_f16_dyn(const GemvArgs& a, hipStream_t s);
+hipError_t launch_gemv_f16_side_dyn(const GemvArgs& a, hipStream_t s);
+
+static hipError_t launch_valu(bool f16, const GemvArgs& a, hipStream_t s);
 
 hipError_t launch_gemv(bool f16, const GemvArgs& a, hipStream_t s) {
     if (a.nseg < 1 || a.nseg > kMaxSeg || a.nside < 0 || a.nside > kMaxSide || a.nattn < 0)
@@ -26,6 +32,21 @@ hipError_t launch_gemv(bool f16, const GemvArgs& a, hipStream_t s) {
         return launch_gemv_mfma(a, a.mfma_part, s);
     }
     if (a.B > kMaxBatch) return hipErrorInvalidValue;
+    GemvArgs d = a;
+    d.dyn = false;
+    if (a.nseg > 1 && a.nattn == 0) {
+        bool counted = false, same = true;
+        for (int i = 0; i < a.nseg; ++i) {
+            counted = counted || a.seg[i].list.count != nullptr;
+            const RowInput &p = a.seg[i].in, &q = a.seg[0].in;
+            same = same && p.y == q.y && p.x == q.x && p.stats == q.stats && p.ntiles == q.ntiles && p.eps == q.eps;
+        }
+        d.dyn = counted && same;
+    }
+    return launch_valu(f16, d, s);
+}
+
+static hipError_t launch_valu(bool f16, const GemvArgs& a, hipStream_t s) {
     bool long_rows = false;
     for (int i = 0; i < a.nside; ++i) long_rows = long_rows || a.side[i].n_out > kShortRows;
     if (long_rows && (a.nattn > 0 || a.B > 1)) {
@@ -35,10 +56,17 @@ hipError_t launch_gemv(bool f16, const GemvArgs& a, hipStream_t s) {
         if (e != hipSuccess) return e;
         GemvArgs b = a;
         b.nside = 0;
+        if (a.dyn) return f16 ? launch_gemv_f16_dyn(b, s) : launch_gemv_f32_dyn(b, s);
         return f16 ? launch_gemv_f16(b, s) : launch_gemv_f32(b, s);
     }
-    if (f16) return long_rows ? launch_gemv_f16_side(a, s) : launch_gemv_f16(a, s);
-    return long_rows ? launch_gemv_f32_side(a, s) : launch_gemv_f32(a, s);
+    if (a.dyn && (long_rows || a.nside == 0)) {
+        if (f16) return long_rows ? launch_gemv_f16_side_dyn(a, s) : launch_gemv_f16_dyn(a, s);
+        return long_rows ? launch_gemv_f32_side_dyn(a, s) : launch_gemv_f32_dyn(a, s);
+    }
+    GemvArgs b = a;
+    b.dyn = false;  // short-row side selections run in the static form
+    if (f16) return long_rows ? launch_gemv_f16_side(b, s) : launch_gemv_f16(b, s);
+    return long_rows ? launch_gemv_f32_side(b, s) : launch_gemv_f32(b, s);
 }
 
 }  // namespace djv

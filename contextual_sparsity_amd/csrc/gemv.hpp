@@ -166,15 +166,17 @@ template <int MODE> struct BlockOf { static constexpr int value = MODE == 2 ? 10
 // unconditionally and the weight buffers keep fixed registers across loop trips.
 static __device__ const Vec16 g_zero_row[2048] = {};
 
-// Weights of one group of G rows in flight, with the rows' units and biases (scalar).
+// Weights of one group of G rows in flight, with the rows' units and biases (scalar), and
+// the group's segment and index inside it.
 template <int G, int NV>
 struct Group {
     Vec16 w[G][NV];
     int unit[G];
     float bias[G];
+    int sg, lg;
 };
 
-template <typename T, int TS, int NV, int NB, int G, int MODE>
+template <typename T, int TS, int NV, int NB, int G, int MODE, bool DYN>
 __global__ __launch_bounds__(BlockOf<MODE>::value) void gemv_kernel(GemvArgs a) {
     constexpr int kThreads = BlockOf<MODE>::value;
     int bid = (int)blockIdx.x;
@@ -208,22 +210,42 @@ __global__ __launch_bounds__(BlockOf<MODE>::value) void gemv_kernel(GemvArgs a) 
     // is uniform over the wave and lives in scalar registers
     const int tm = __builtin_amdgcn_readfirstlane(tid / TS);
     const int lt = tid % TS, wv = lt / kWave, ln = tid % kWave;
-    int sg = 0;
+    // Static split: each block belongs to one segment and its teams stride over that
+    // segment's groups.  Dynamic split (DYN: segments that read the same input, with device
+    // counts): all GEMV blocks form one pool whose teams stride over the groups of all
+    // segments, laid end to end by the counts, so a short list does not leave its blocks
+    // idle while another segment's few blocks carry the launch.
+    int sg0 = 0;
+    int rows_seg[kMaxSeg] = {0, 0, 0}, groups_seg[kMaxSeg] = {0, 0, 0};
+    int groups, stride;
+    if constexpr (DYN) {
+        int pool = 0;
+        groups = 0;
 #pragma unroll
-    for (int i = 0; i + 1 < kMaxSeg; ++i)
-        if (sg == i && i + 1 < a.nseg && bid >= a.seg[i].blocks) {
-            bid -= a.seg[i].blocks;
-            sg = i + 1;
-        }
-    const GemvSeg S = a.seg[sg];
+        for (int i = 0; i < kMaxSeg; ++i)
+            if (i < a.nseg) {
+                rows_seg[i] = read_count_uniform(a.seg[i].list, a.flags) * a.seg[i].rpu;
+                groups_seg[i] = (rows_seg[i] + G - 1) / G;
+                groups += groups_seg[i];
+                pool += a.seg[i].blocks;
+            }
+        stride = pool * NT;
+    } else {
+#pragma unroll
+        for (int i = 0; i + 1 < kMaxSeg; ++i)
+            if (sg0 == i && i + 1 < a.nseg && bid >= a.seg[i].blocks) {
+                bid -= a.seg[i].blocks;
+                sg0 = i + 1;
+            }
+    }
+    const GemvSeg S = a.seg[sg0];  // the block's segment (static), or the shared input (DYN)
+    if constexpr (!DYN) {
+        rows_seg[0] = read_count_uniform(S.list, a.flags) * S.rpu;
+        groups = (rows_seg[0] + G - 1) / G;
+        stride = S.blocks * NT;  // groups between a team's consecutive groups
+    }
     const int nvec = a.cols / E;
-    const int count = read_count_uniform(S.list, a.flags);
-    const int rows = count * S.rpu;
-    const int groups = (rows + G - 1) / G;
-    const int stride = S.blocks * NT;  // groups between a team's consecutive groups
-    const char* Wb = reinterpret_cast<const char*>(S.W);
     const size_t row_bytes = (size_t)a.cols * sizeof(T);
-    const bool with_bias = S.epi == kEpiBiasRelu;
 
     // units (and biases) come from scalar loads and row addresses are scalar, so the
     // weight loads of a group depend on no vector load (nothing waits for the other
@@ -234,24 +256,45 @@ __global__ __launch_bounds__(BlockOf<MODE>::value) void gemv_kernel(GemvArgs a) 
     const uint32_t lane_off = (uint32_t)lt * 16u;
     const uint32_t last_off = (uint32_t)(min(lt + TS * (NV - 1), nvec - 1) - TS * (NV - 1)) * 16u;
     gchar* zero_row = uniform_ptr(g_zero_row);
-    auto load_group = [&](Group<G, NV>& q, int grp) {
+    auto load_from = [&](Group<G, NV>& q, const GemvSeg& Q, int rows) {
+        const bool with_bias = Q.epi == kEpiBiasRelu;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            const int r = grp * G + g;
+            const int r = q.lg * G + g;
             int unit = -1;
-            if (r < rows) unit = unit_of_uniform(S.list, r / S.rpu, a.flags);
+            if (r < rows) unit = unit_of_uniform(Q.list, r / Q.rpu, a.flags);
             q.unit[g] = unit;
-            q.bias[g] = (with_bias && unit >= 0) ? load_bias<T>(S.bias, unit) : 0.f;
+            q.bias[g] = (with_bias && unit >= 0) ? load_bias<T>(Q.bias, unit) : 0.f;
         }
+        const char* Wb = reinterpret_cast<const char*>(Q.W);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            const int r = grp * G + g;
-            const int u = r / S.rpu;
-            const size_t row = (size_t)(q.unit[g] < 0 ? 0 : q.unit[g]) * S.rpu + (r - u * S.rpu);
+            const int r = q.lg * G + g;
+            const int u = r / Q.rpu;
+            const size_t row = (size_t)(q.unit[g] < 0 ? 0 : q.unit[g]) * Q.rpu + (r - u * Q.rpu);
             gchar* rp = q.unit[g] < 0 ? zero_row : uniform_ptr(Wb + row * row_bytes);
 #pragma unroll
             for (int i = 0; i < NV; ++i)
                 q.w[g][i] = ldg16_nt_at(rp + (size_t)16 * TS * i, i + 1 < NV ? lane_off : last_off);
+        }
+    };
+    auto load_group = [&](Group<G, NV>& q, int grp) {
+        if constexpr (DYN) {
+            // group grp of the launch -> segment and index inside it
+            int sg = 0, lg = grp;
+#pragma unroll
+            for (int i = 0; i + 1 < kMaxSeg; ++i)
+                if (sg == i && i + 1 < a.nseg && lg >= groups_seg[i]) {
+                    lg -= groups_seg[i];
+                    sg = i + 1;
+                }
+            q.sg = sg;
+            q.lg = lg;
+            load_from(q, a.seg[sg], rows_seg[sg]);
+        } else {
+            q.sg = 0;
+            q.lg = grp;
+            load_from(q, S, rows_seg[0]);
         }
     };
 
@@ -294,6 +337,7 @@ __global__ __launch_bounds__(BlockOf<MODE>::value) void gemv_kernel(GemvArgs a) 
     // barriers stay uniform.
     auto step = [&](Group<G, NV>& q, int base, int parity) {
         const int cur = base + tm;
+        const int qsg = q.sg, qlg = q.lg;  // this group's segment and index inside it
         float acc[G][NB];
         int unit[G];
         float bias[G];
@@ -329,8 +373,12 @@ __global__ __launch_bounds__(BlockOf<MODE>::value) void gemv_kernel(GemvArgs a) 
                             bs = bias[g];
                         }
                 const int g = ln / NB, b = ln % NB;
-                const int r = cur * G + g;
-                if (r < rows && b < a.B) epilogue<T>(a, S, r, b, v, un, bs);
+                const int r = qlg * G + g;
+                if constexpr (DYN) {
+                    if (r < rows_seg[qsg] && b < a.B) epilogue<T>(a, a.seg[qsg], r, b, v, un, bs);
+                } else {
+                    if (r < rows_seg[0] && b < a.B) epilogue<T>(a, S, r, b, v, un, bs);
+                }
             }
         } else {
             // wave sums through LDS, double-buffered so one barrier per group suffices
@@ -355,8 +403,12 @@ __global__ __launch_bounds__(BlockOf<MODE>::value) void gemv_kernel(GemvArgs a) 
                         bs = bias[g];
                     }
                 const int g = lt / NB, b = lt % NB;
-                const int r = cur * G + g;
-                if (r < rows && b < a.B) epilogue<T>(a, S, r, b, v, un, bs);
+                const int r = qlg * G + g;
+                if constexpr (DYN) {
+                    if (r < rows_seg[qsg] && b < a.B) epilogue<T>(a, a.seg[qsg], r, b, v, un, bs);
+                } else {
+                    if (r < rows_seg[0] && b < a.B) epilogue<T>(a, S, r, b, v, un, bs);
+                }
             }
         }
     };
@@ -370,12 +422,12 @@ __global__ __launch_bounds__(BlockOf<MODE>::value) void gemv_kernel(GemvArgs a) 
     }
 }
 
-template <typename T, int TS, int NV, int NB, int G, int MODE>
+template <typename T, int TS, int NV, int NB, int G, int MODE, bool DYN>
 int blocks_per_cu() {
     static const int occ = [] {
         int n = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &n, reinterpret_cast<const void*>(&gemv_kernel<T, TS, NV, NB, G, MODE>),
+                &n, reinterpret_cast<const void*>(&gemv_kernel<T, TS, NV, NB, G, MODE, DYN>),
                 BlockOf<MODE>::value, 0) !=
                 hipSuccess ||
             n < 1)
@@ -390,10 +442,10 @@ constexpr int kOversub = 1;
 
 // Shares the resident blocks among the segments in proportion to their groups of rows
 // (at least one each) and launches.
-template <typename T, int TS, int NV, int NB, int G, int MODE>
+template <typename T, int TS, int NV, int NB, int G, int MODE, bool DYN>
 hipError_t launch_shape(GemvArgs a, hipStream_t s) {
     constexpr int NT = BlockOf<MODE>::value / TS;
-    const int slots = blocks_per_cu<T, TS, NV, NB, G, MODE>() * device_cus() * kOversub;
+    const int slots = blocks_per_cu<T, TS, NV, NB, G, MODE, DYN>() * device_cus() * kOversub;
     if (MODE != 1) a.nattn = 0;
     if (MODE == 0) a.nside = 0;
     // the prefix blocks (attention chunks, selections) are short; when they fill most of
@@ -420,16 +472,16 @@ hipError_t launch_shape(GemvArgs a, hipStream_t s) {
     }
     dim3 grid(total + nprefix);
     prof_begin(a.prof, s);
-    hipLaunchKernelGGL((gemv_kernel<T, TS, NV, NB, G, MODE>), grid, dim3(BlockOf<MODE>::value), 0, s, a);
+    hipLaunchKernelGGL((gemv_kernel<T, TS, NV, NB, G, MODE, DYN>), grid, dim3(BlockOf<MODE>::value), 0, s, a);
     prof_end(a.prof, s);
     return hipGetLastError();
 }
 
-template <typename T, int TS, int NB, int MODE>
+template <typename T, int TS, int NB, int MODE, bool DYN>
 hipError_t dispatch_nv(const GemvArgs& a, int nv, hipStream_t s) {
 #define DJV_GEMV_CASE(NVV, GG) \
     case NVV:                  \
-        return launch_shape<T, TS, NVV, NB, GG, MODE>(a, s);
+        return launch_shape<T, TS, NVV, NB, GG, MODE, DYN>(a, s);
     if constexpr (TS == 64) {
         switch (nv) {
             DJV_GEMV_CASE(1, 4)
@@ -472,7 +524,7 @@ hipError_t dispatch_nv(const GemvArgs& a, int nv, hipStream_t s) {
 }
 
 // Chooses the team size, vectors per thread and rows per team, and launches.
-template <typename T, int MODE>
+template <typename T, int MODE, bool DYN = false>
 hipError_t dispatch(const GemvArgs& a, hipStream_t s) {
     constexpr int E = WTraits<T>::kPerVec;
     if (a.nseg < 1 || a.nseg > kMaxSeg || a.nside < 0 || a.nside > kMaxSide) return hipErrorInvalidValue;
@@ -485,16 +537,16 @@ hipError_t dispatch(const GemvArgs& a, hipStream_t s) {
         // long-row side selections are compiled for one batch row only (the launcher runs
         // them separately otherwise)
         if (nb != 1) return hipErrorInvalidValue;
-        return small ? dispatch_nv<T, 64, 1, MODE>(a, nv, s) : dispatch_nv<T, 256, 1, MODE>(a, nv, s);
+        return small ? dispatch_nv<T, 64, 1, MODE, DYN>(a, nv, s) : dispatch_nv<T, 256, 1, MODE, DYN>(a, nv, s);
     } else {
         if (small) {
-            if (nb == 1) return dispatch_nv<T, 64, 1, MODE>(a, nv, s);
-            if (nb == 2) return dispatch_nv<T, 64, 2, MODE>(a, nv, s);
-            return dispatch_nv<T, 64, 4, MODE>(a, nv, s);
+            if (nb == 1) return dispatch_nv<T, 64, 1, MODE, DYN>(a, nv, s);
+            if (nb == 2) return dispatch_nv<T, 64, 2, MODE, DYN>(a, nv, s);
+            return dispatch_nv<T, 64, 4, MODE, DYN>(a, nv, s);
         }
-        if (nb == 1) return dispatch_nv<T, 256, 1, MODE>(a, nv, s);
-        if (nb == 2) return dispatch_nv<T, 256, 2, MODE>(a, nv, s);
-        return dispatch_nv<T, 256, 4, MODE>(a, nv, s);
+        if (nb == 1) return dispatch_nv<T, 256, 1, MODE, DYN>(a, nv, s);
+        if (nb == 2) return dispatch_nv<T, 256, 2, MODE, DYN>(a, nv, s);
+        return dispatch_nv<T, 256, 4, MODE, DYN>(a, nv, s);
     }
 }
 

@@ -138,6 +138,48 @@ def test_stack_small(lookahead):
     assert np.array_equal(host(x), host(x2))
 
 
+# Sets whose sizes are known only on the device (threshold selection, or the union of
+# per-token top-k sets) make the fused projection launches lay the rows of all their
+# segments end to end and share every block among them.
+@pytest.mark.parametrize("B,mode,t", [(1, dj.DJV_THRESHOLD, 0.6), (3, dj.DJV_THRESHOLD, 0.7),
+                                      (3, dj.DJV_TOPK, None), (2, dj.DJV_TOPK, None)])
+def test_stack_device_counts(B, mode, t):
+    print(f"lookahead stack with device counts B={B} mode={mode}", flush=True)
+    s = synth.LayerShape(d=1032, N=1500, h=6, dh=128, n=300, r=136, dtype="f16", B=B)
+    if mode == dj.DJV_TOPK:
+        st = Stack(s, 3, 25, k_A=2, k_M=75)
+    else:
+        st = Stack(s, 3, 25, k_A=0, k_M=0, mode=mode, t_A=t, t_M=t)
+    x, tr = st.run(lookahead=True)
+    assert (tr["counts"][:, 1] > 0).all() and (tr["counts"][:, 1] < s.N).all()
+    check_stack(st, host(x), tr, lookahead=True)
+    x2, _ = st.run(lookahead=True)
+    assert np.array_equal(host(x), host(x2))
+
+
+def test_stack_threshold_larger_shape():
+    print("lookahead threshold stack d=4096", flush=True)
+    s = synth.LayerShape(d=4096, N=16384, h=32, dh=128, n=512, r=1024, dtype="f16")
+    st = Stack(s, 2, 26, k_A=0, k_M=0, mode=dj.DJV_THRESHOLD, t_A=0.6, t_M=0.7)
+    x, tr = st.run(lookahead=True)
+    assert (tr["counts"][:, 1] > 0).all() and (tr["counts"][:, 1] < s.N).all()
+    check_stack(st, host(x), tr, lookahead=True)
+
+
+@pytest.mark.parametrize("t,kept", [(0.999999, "none"), (1e-6, "all")])
+def test_stack_threshold_keeps_none_or_all(t, kept):
+    print(f"lookahead threshold stack keeping {kept}", flush=True)
+    s = synth.LayerShape(d=1032, N=1500, h=6, dh=128, n=300, r=136, dtype="f16")
+    st = Stack(s, 2, 27, k_A=0, k_M=0, mode=dj.DJV_THRESHOLD, t_A=t, t_M=t)
+    x, tr = st.run(lookahead=True)
+    want = (0, 0) if kept == "none" else (s.h, s.N)
+    assert (tr["counts"] == np.array(want)).all(), tr["counts"]
+    check_stack(st, host(x), tr, lookahead=True)
+    if kept == "none":
+        # nothing computed: each layer passes its input through unchanged
+        assert np.array_equal(host(x), host(st.x0))
+
+
 def test_dense_stack_matches_oracle():
     s = synth.LayerShape(d=1032, N=1500, h=6, dh=128, n=300, r=136, dtype="f16")
     st = Stack(s, 2, 24, k_A=2, k_M=75)

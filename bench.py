@@ -405,6 +405,19 @@ def main(argv=None) -> int:
     log("warm-up done")
     ms_step, wall_ms = timed(args.steps)
     log(f"sparse step {ms_step:.3f} ms (wall {wall_ms:.3f} ms)")
+
+    def family_time(fam, n_steps):
+        cap = n_steps * L + 4
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * cap)]
+        dj.dejavu_profile_kernel(fam, evs)
+        for _ in range(n_steps):
+            step()
+        used = dj.dejavu_profile_count()
+        torch.cuda.synchronize()
+        dj.dejavu_profile_kernel("off")
+        d = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(used)]
+        return sum(d) / max(1, len(d)), used
+
     if thr is not None:
         counts = torch.zeros(L, 2, dtype=torch.int32, device=dev)
         x.copy_(x0)
@@ -424,6 +437,10 @@ def main(argv=None) -> int:
                "kept_neurons": {"mean": round(c[:, 1].mean().item(), 1), "min": int(c[:, 1].min()),
                                 "max": int(c[:, 1].max())},
                "bytes_per_layer_mean": round(step_bytes_t / L)}
+        if args.breakdown:
+            out["kernels_us"] = {fam: round(family_time(fam, max(3, args.steps // 4))[0] * 1e3, 2)
+                                 for fam in ("qkv", "mlp_up", "mlp_down", "o_proj", "attn", "pred_1",
+                                             "pred_2", "select")}
         print(json.dumps(out), flush=True)
         return 0
     lb = layer_bytes(s, k_A, k_M)
@@ -437,17 +454,6 @@ def main(argv=None) -> int:
     p1_bytes = 2 * s.r * s.d * e
     k1_bytes = lb["qkv"] + p1_bytes * (L - 1) / L   # the last layer has no next layer
 
-    def family_time(fam, n_steps):
-        cap = n_steps * L + 4
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * cap)]
-        dj.dejavu_profile_kernel(fam, evs)
-        for _ in range(n_steps):
-            step()
-        used = dj.dejavu_profile_count()
-        torch.cuda.synchronize()
-        dj.dejavu_profile_kernel("off")
-        d = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(used)]
-        return sum(d) / max(1, len(d)), used
 
     qkv_ms, qkv_n = family_time("qkv", args.steps)
     qkv_gbs = k1_bytes / (qkv_ms * 1e-3) / 1e9

@@ -112,8 +112,32 @@ __device__ __forceinline__ void row_moments(const RowInput& in, int cols, int b,
 }
 
 // Writes the result of visited row r (weight unit `unit`, -1 when skipped) for batch row b.
+// What a group's weight loads need of its segment, and what its stores need: small
+// enough to keep every segment's copy in scalar registers and pick one by a uniform select.
+struct SegRows {
+    const char* W;
+    const int32_t* idx;
+    const void* bias;
+    int units, rpu, with_bias;
+};
+struct SegOut {
+    float* out;
+    int ld, epi, rpu, cap;
+};
+__device__ __forceinline__ SegRows seg_rows(const GemvSeg& S) {
+    return {reinterpret_cast<const char*>(S.W), S.list.idx, S.bias, S.list.units, S.rpu,
+            S.epi == kEpiBiasRelu};
+}
+__device__ __forceinline__ SegOut seg_out(const GemvSeg& S) {
+    return {S.out, S.ld, S.epi, S.rpu, S.list.cap};
+}
+template <typename Seg>
+__device__ __forceinline__ Seg pick3(int i, const Seg& s0, const Seg& s1, const Seg& s2) {
+    return i == 0 ? s0 : (i == 1 ? s1 : s2);
+}
+
 template <typename T>
-__device__ __forceinline__ void epilogue(const GemvArgs& a, const GemvSeg& S, int r, int b, float acc,
+__device__ __forceinline__ void epilogue(const GemvArgs& a, const SegOut& S, int r, int b, float acc,
                                          int unit, float bias) {
     switch (S.epi) {
     case kEpiStore:
@@ -130,7 +154,7 @@ __device__ __forceinline__ void epilogue(const GemvArgs& a, const GemvSeg& S, in
         const int u = r / S.rpu, sub = r - u * S.rpu;
         const int part = sub / a.dh, c = sub - part * a.dh;
         if (part == 0) {
-            S.out[((size_t)b * S.list.cap + u) * a.dh + c] = acc;
+            S.out[((size_t)b * S.cap + u) * a.dh + c] = acc;
         } else {
             T* cache = reinterpret_cast<T*>(part == 1 ? a.Kc : a.Vc);
             cache[(((size_t)b * a.h + unit) * a.n_cap + a.n) * a.dh + c] = to_store<T>(acc);
@@ -239,6 +263,8 @@ __global__ __launch_bounds__(BlockOf<MODE>::value) void gemv_kernel(GemvArgs a) 
             }
     }
     const GemvSeg S = a.seg[sg0];  // the block's segment (static), or the shared input (DYN)
+    const SegRows R0 = seg_rows(S), R1 = seg_rows(a.seg[1]), R2 = seg_rows(a.seg[2]);
+    const SegOut O0 = seg_out(S), O1 = seg_out(a.seg[1]), O2 = seg_out(a.seg[2]);
     if constexpr (!DYN) {
         rows_seg[0] = read_count_uniform(S.list, a.flags) * S.rpu;
         groups = (rows_seg[0] + G - 1) / G;
@@ -256,23 +282,22 @@ __global__ __launch_bounds__(BlockOf<MODE>::value) void gemv_kernel(GemvArgs a) 
     const uint32_t lane_off = (uint32_t)lt * 16u;
     const uint32_t last_off = (uint32_t)(min(lt + TS * (NV - 1), nvec - 1) - TS * (NV - 1)) * 16u;
     gchar* zero_row = uniform_ptr(g_zero_row);
-    auto load_from = [&](Group<G, NV>& q, const GemvSeg& Q, int rows) {
-        const bool with_bias = Q.epi == kEpiBiasRelu;
+    auto load_from = [&](Group<G, NV>& q, const SegRows& Q, int rows) {
+        const UnitList list{Q.idx, nullptr, 0, Q.units};
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const int r = q.lg * G + g;
             int unit = -1;
-            if (r < rows) unit = unit_of_uniform(Q.list, r / Q.rpu, a.flags);
+            if (r < rows) unit = unit_of_uniform(list, r / Q.rpu, a.flags);
             q.unit[g] = unit;
-            q.bias[g] = (with_bias && unit >= 0) ? load_bias<T>(Q.bias, unit) : 0.f;
+            q.bias[g] = (Q.with_bias && unit >= 0) ? load_bias<T>(Q.bias, unit) : 0.f;
         }
-        const char* Wb = reinterpret_cast<const char*>(Q.W);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const int r = q.lg * G + g;
             const int u = r / Q.rpu;
             const size_t row = (size_t)(q.unit[g] < 0 ? 0 : q.unit[g]) * Q.rpu + (r - u * Q.rpu);
-            gchar* rp = q.unit[g] < 0 ? zero_row : uniform_ptr(Wb + row * row_bytes);
+            gchar* rp = q.unit[g] < 0 ? zero_row : uniform_ptr(Q.W + row * row_bytes);
 #pragma unroll
             for (int i = 0; i < NV; ++i)
                 q.w[g][i] = ldg16_nt_at(rp + (size_t)16 * TS * i, i + 1 < NV ? lane_off : last_off);
@@ -290,11 +315,11 @@ __global__ __launch_bounds__(BlockOf<MODE>::value) void gemv_kernel(GemvArgs a) 
                 }
             q.sg = sg;
             q.lg = lg;
-            load_from(q, a.seg[sg], rows_seg[sg]);
+            load_from(q, pick3(sg, R0, R1, R2), pick3(sg, rows_seg[0], rows_seg[1], rows_seg[2]));
         } else {
             q.sg = 0;
             q.lg = grp;
-            load_from(q, S, rows_seg[0]);
+            load_from(q, R0, rows_seg[0]);
         }
     };
 
@@ -375,9 +400,10 @@ __global__ __launch_bounds__(BlockOf<MODE>::value) void gemv_kernel(GemvArgs a) 
                 const int g = ln / NB, b = ln % NB;
                 const int r = qlg * G + g;
                 if constexpr (DYN) {
-                    if (r < rows_seg[qsg] && b < a.B) epilogue<T>(a, a.seg[qsg], r, b, v, un, bs);
+                    if (r < pick3(qsg, rows_seg[0], rows_seg[1], rows_seg[2]) && b < a.B)
+                        epilogue<T>(a, pick3(qsg, O0, O1, O2), r, b, v, un, bs);
                 } else {
-                    if (r < rows_seg[0] && b < a.B) epilogue<T>(a, S, r, b, v, un, bs);
+                    if (r < rows_seg[0] && b < a.B) epilogue<T>(a, O0, r, b, v, un, bs);
                 }
             }
         } else {
@@ -405,9 +431,10 @@ __global__ __launch_bounds__(BlockOf<MODE>::value) void gemv_kernel(GemvArgs a) 
                 const int g = lt / NB, b = lt % NB;
                 const int r = qlg * G + g;
                 if constexpr (DYN) {
-                    if (r < rows_seg[qsg] && b < a.B) epilogue<T>(a, a.seg[qsg], r, b, v, un, bs);
+                    if (r < pick3(qsg, rows_seg[0], rows_seg[1], rows_seg[2]) && b < a.B)
+                        epilogue<T>(a, pick3(qsg, O0, O1, O2), r, b, v, un, bs);
                 } else {
-                    if (r < rows_seg[0] && b < a.B) epilogue<T>(a, S, r, b, v, un, bs);
+                    if (r < rows_seg[0] && b < a.B) epilogue<T>(a, O0, r, b, v, un, bs);
                 }
             }
         }

@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256) void gemv_mfma_finalize_kernel(GemvArgs a, Mfm
     const int unit = unit_of(S.list, r / S.rpu, a.flags);
     float bias = 0.f;
     if (S.epi == kEpiBiasRelu && unit >= 0) bias = to_f32<T>(reinterpret_cast<const T*>(S.bias)[unit]);
-    gemv_detail::epilogue<T>(a, S, r, b, acc, unit, bias);
+    gemv_detail::epilogue<T>(a, gemv_detail::seg_out(S), r, b, acc, unit, bias);
 }
 
 // Slices of a row of `cols` columns for batch padding bpad: as few as the LDS allows, of

@@ -7,7 +7,7 @@ lookahead schedule) or each layer predicts its own sets in order (serial schedul
 from __future__ import annotations
 
 from dataclasses import dataclass
-from typing import Dict
+from typing import Dict, Tuple
 
 from .synth import LayerShape
 
@@ -69,3 +69,11 @@ WORKLOADS: Dict[str, Workload] = {
 SWEEP_PCT_M = (1, 2, 5, 10, 25, 50, 100)
 SWEEP_PCT_A = (10, 20, 50, 100)
 SWEEP_BATCH = (1, 2, 4, 8, 16, 32)
+
+
+def shard_range(n: int, g: int, i: int) -> Tuple[int, int]:
+    """Units [lo, hi) of shard i when n units are split over g shards in contiguous
+    ranges, the first n % g shards one unit longer."""
+    base, extra = divmod(n, g)
+    lo = i * base + min(i, extra)
+    return lo, lo + base + (1 if i < extra else 0)

@@ -244,6 +244,15 @@ int cap_of(int mode, int k, int n, int B) {
     return c < n ? (int)c : n;
 }
 
+// A tensor-parallel shard of a model: its predictors score all heads / neurons and select
+// among them; its weights, caches and lists cover its own range (h heads from h_offset,
+// N neurons from N_offset).  Unsharded: the range is everything.
+int heads_total(const djv_model& m) { return m.h_total > 0 ? m.h_total : m.h; }
+int neurons_total(const djv_model& m) { return m.N_total > 0 ? m.N_total : m.N; }
+bool sharded(const djv_model& m) { return m.h_total > 0 || m.N_total > 0; }
+int capA_of(const djv_model& m) { return std::min(cap_of(m.mode, m.k_A, heads_total(m), m.B), m.h); }
+int capM_of(const djv_model& m) { return std::min(cap_of(m.mode, m.k_M, neurons_total(m), m.B), m.N); }
+
 // Activation state and scratch of a layer or a stack of layers.
 struct LayerWs {
     float* xs[2];                     // residual-stream ring: inputs of layers 1..L-1
@@ -269,8 +278,8 @@ LayerWs plan_layer(Arena& A, const djv_model& m, bool dense) {
     w.s_in = A.take<float2>((size_t)m.B * w.tiles);
     w.xm = A.take<float>((size_t)m.B * m.d);
     w.sm = A.take<float2>((size_t)m.B * w.tiles);
-    const int capA = dense ? m.h : cap_of(m.mode, m.k_A, m.h, m.B);
-    const int capM = dense ? m.N : cap_of(m.mode, m.k_M, m.N, m.B);
+    const int capA = dense ? m.h : capA_of(m);
+    const int capM = dense ? m.N : capM_of(m);
     for (int i = 0; i < 2; ++i) {
         w.idxA[i] = A.take<int32_t>(m.h);
         w.cntA[i] = A.take<int32_t>(1);
@@ -279,14 +288,14 @@ LayerWs plan_layer(Arena& A, const djv_model& m, bool dense) {
     }
     // one matrix-core scratch for every launch of the layer; its largest launches: Q/K/V
     // with both P1, both P2, MLP up
-    const long long rows = std::max({(long long)capA * 3 * m.dh + 2LL * m.r, (long long)m.h + m.N,
-                                     (long long)capM});
+    const long long rows = std::max({(long long)capA * 3 * m.dh + 2LL * m.r,
+                                     (long long)heads_total(m) + neurons_total(m), (long long)capM});
     w.mf = plan_mfma(A, layer_wide(m), m.B, rows, std::max(m.d, m.r));
     w.mha = plan_mha(A, m.B, m.d, m.dh, capA, m.n_cap, f16, true, &w.mf);
     w.mlp = plan_mlp(A, m.B, m.d, capM, f16, true, &w.mf);
     if (!dense) {
-        w.predA = plan_predict(A, m.B, m.d, m.r, m.h, true, true, &w.mf);
-        w.predM = plan_predict(A, m.B, m.d, m.r, m.N, true, true, &w.mf);
+        w.predA = plan_predict(A, m.B, m.d, m.r, heads_total(m), true, true, &w.mf);
+        w.predM = plan_predict(A, m.B, m.d, m.r, neurons_total(m), true, true, &w.mf);
     } else {
         w.predA = w.predM = PredWs{nullptr, nullptr, nullptr, w.mf};
     }
@@ -315,6 +324,7 @@ struct PredJob {
     int mode, k; float t;
     int32_t* idx; int32_t* count; float* z;
     const PredWs* w;
+    int lo, hi;  // the units listed: [lo, hi) of the n_out scored, rebased to lo
 };
 
 // GEMV segments of the layer's weight streams.
@@ -332,7 +342,7 @@ GemvSeg seg_second(const PredJob& j) {
 }
 SelectJob select_job(const PredJob& j) {
     return SelectJob{j.z, j.n_out, j.mode, j.k, j.mode == DJV_THRESHOLD ? tau_key(j.t) : 0u,
-                     j.w->bits, j.idx, j.count};
+                     j.w->bits, j.idx, j.count, j.lo, j.hi};
 }
 GemvSeg seg_qkv(const void* Wqkv, const UnitList& heads, int dh, const RowInput& in, float* q) {
     GemvSeg S{};
@@ -461,8 +471,14 @@ djv_status check_model(const djv_model* m) {
                     <= kAttnMaxChunks, DJV_EUNSUPPORTED, "n_cap = %d is too long", m->n_cap);
     DJV_REQUIRE(std::isfinite(m->scale), DJV_EINVAL, "scale must be finite");
     DJV_REQUIRE(m->eps > 0.f && std::isfinite(m->eps), DJV_EINVAL, "eps must be > 0");
-    DJV_TRY(check_select(m->h, m->mode, m->k_A, m->t_A, "head selection"));
-    DJV_TRY(check_select(m->N, m->mode, m->k_M, m->t_M, "neuron selection"));
+    DJV_REQUIRE(m->h_total > 0 ? (m->h_offset >= 0 && m->h_offset + (long long)m->h <= m->h_total)
+                               : (m->h_total == 0 && m->h_offset == 0),
+                DJV_EINVAL, "head shard: need 0 <= h_offset and h_offset + h <= h_total (or all 0)");
+    DJV_REQUIRE(m->N_total > 0 ? (m->N_offset >= 0 && m->N_offset + (long long)m->N <= m->N_total)
+                               : (m->N_total == 0 && m->N_offset == 0),
+                DJV_EINVAL, "neuron shard: need 0 <= N_offset and N_offset + N <= N_total (or all 0)");
+    DJV_TRY(check_select(heads_total(*m), m->mode, m->k_A, m->t_A, "head selection"));
+    DJV_TRY(check_select(neurons_total(*m), m->mode, m->k_M, m->t_M, "neuron selection"));
     return DJV_OK;
 }
 
@@ -502,7 +518,7 @@ djv_status copy_async(void* dst, const void* src, size_t bytes, hipStream_t s) {
 djv_status trace_sets(const djv_trace* tr, const djv_model& m, int l, const LayerWs& w, int buf,
                       hipStream_t s) {
     if (!tr) return DJV_OK;
-    const int capA = cap_of(m.mode, m.k_A, m.h, m.B), capM = cap_of(m.mode, m.k_M, m.N, m.B);
+    const int capA = capA_of(m), capM = capM_of(m);
     if (tr->sets_A) DJV_TRY(copy_async(tr->sets_A + (size_t)l * m.h, w.idxA[buf], capA * 4, s));
     if (tr->sets_M) DJV_TRY(copy_async(tr->sets_M + (size_t)l * m.N, w.idxM[buf], capM * 4, s));
     if (tr->counts) {
@@ -519,21 +535,21 @@ djv_status trace_x(const djv_trace* tr, const djv_model& m, int l, const float* 
 
 // Score buffers of layer l: the trace's when it asks for them, else the workspace's.
 float* zA_of(const djv_trace* tr, const djv_model& m, int l, const LayerWs& w) {
-    return (tr && tr->z_A) ? tr->z_A + (size_t)l * m.B * m.h : w.predA.z;
+    return (tr && tr->z_A) ? tr->z_A + (size_t)l * m.B * heads_total(m) : w.predA.z;
 }
 float* zM_of(const djv_trace* tr, const djv_model& m, int l, const LayerWs& w) {
-    return (tr && tr->z_M) ? tr->z_M + (size_t)l * m.B * m.N : w.predM.z;
+    return (tr && tr->z_M) ? tr->z_M + (size_t)l * m.B * neurons_total(m) : w.predM.z;
 }
 
 PredJob job_A(const djv_model& m, const djv_layer& L, const LayerWs& w, int buf,
               const djv_trace* tr, int l) {
-    return PredJob{L.P1_A, L.P2_A, m.h, m.mode, m.k_A, m.t_A, w.idxA[buf], w.cntA[buf],
-                   zA_of(tr, m, l, w), &w.predA};
+    return PredJob{L.P1_A, L.P2_A, heads_total(m), m.mode, m.k_A, m.t_A, w.idxA[buf], w.cntA[buf],
+                   zA_of(tr, m, l, w), &w.predA, m.h_offset, m.h_offset + m.h};
 }
 PredJob job_M(const djv_model& m, const djv_layer& L, const LayerWs& w, int buf,
               const djv_trace* tr, int l) {
-    return PredJob{L.P1_M, L.P2_M, m.N, m.mode, m.k_M, m.t_M, w.idxM[buf], w.cntM[buf],
-                   zM_of(tr, m, l, w), &w.predM};
+    return PredJob{L.P1_M, L.P2_M, neurons_total(m), m.mode, m.k_M, m.t_M, w.idxM[buf], w.cntM[buf],
+                   zM_of(tr, m, l, w), &w.predM, m.N_offset, m.N_offset + m.N};
 }
 
 // Input and output of layer l in a stack of L: layer 0 reads the caller's x, the last
@@ -552,9 +568,10 @@ LayerIO layer_io(float* x, const LayerWs& w, int l, int L) {
 }
 
 // Device count of a selected list, or nullptr when it is known on the host to equal the
-// capacity (top-k with one sequence keeps exactly k), which saves kernels a dependent read.
+// capacity (top-k with one sequence keeps exactly k, unless a shard keeps only its part of
+// them), which saves kernels a dependent read.
 const int32_t* count_of(const djv_model& m, const int32_t* count) {
-    return (m.mode == DJV_TOPK && m.B == 1) ? nullptr : count;
+    return (m.mode == DJV_TOPK && m.B == 1 && !sharded(m)) ? nullptr : count;
 }
 
 // Attention then MLP of layer l with the sets in buffer `buf`.  With serial set, the
@@ -564,7 +581,7 @@ djv_status layer_body(const djv_model& m, const djv_layer& L, const LayerIO& io,
     const bool f16 = m.wt == DJV_F16;
     DJV_TRY(run_mha(f16, m.B, m.d, m.h, m.dh, m.n, m.n_cap, ln_input(io.x_in, io.s_in, w, m.eps),
                     L.Wqkv, L.Wo, L.Kc, L.Vc, w.idxA[buf], count_of(m, w.cntA[buf]),
-                    cap_of(m.mode, m.k_A, m.h, m.B), m.scale, io.x_in, w.xm, w.sm, w.mha, s));
+                    capA_of(m), m.scale, io.x_in, w.xm, w.sm, w.mha, s));
     if (tr && tr->x_mid)
         DJV_TRY(copy_async(tr->x_mid + (size_t)l * m.B * m.d, w.xm, (size_t)m.B * m.d * 4, s));
     const RowInput in_m = ln_input(w.xm, w.sm, w, m.eps);
@@ -573,7 +590,7 @@ djv_status layer_body(const djv_model& m, const djv_layer& L, const LayerIO& io,
         DJV_TRY(run_predict(f16, m.B, m.d, m.r, in_m, &jm, 1, w.mf, s));
     }
     DJV_TRY(run_mlp(f16, m.B, m.d, m.N, in_m, L.W1, L.b1, L.W2, w.idxM[buf], count_of(m, w.cntM[buf]),
-                    cap_of(m.mode, m.k_M, m.N, m.B), w.xm, io.x_out, io.s_out, w.mlp, s));
+                    capM_of(m), w.xm, io.x_out, io.s_out, w.mlp, s));
     return DJV_OK;
 }
 
@@ -673,8 +690,16 @@ djv_status dejavu_gather_rows(djv_dtype wt, int rpu, int cols, int units, const 
 
 djv_status dejavu_select(int B, int n_out, const float* z, djv_mode mode, int k, float t,
                          int32_t* idx, int32_t* count, void* ws, size_t ws_bytes, void* stream) {
+    return dejavu_select_range(B, n_out, z, mode, k, t, 0, n_out, idx, count, ws, ws_bytes, stream);
+}
+
+djv_status dejavu_select_range(int B, int n_out, const float* z, djv_mode mode, int k, float t,
+                               int lo, int hi, int32_t* idx, int32_t* count, void* ws,
+                               size_t ws_bytes, void* stream) {
     DJV_REQUIRE(B >= 1 && B <= 65535, DJV_EINVAL, "B must lie in [1, 65535] (got %d)", B);
     DJV_TRY(check_select(n_out, mode, k, t, "select"));
+    DJV_REQUIRE(0 <= lo && lo <= hi && hi <= n_out, DJV_EINVAL,
+                "need 0 <= lo <= hi <= n_out (lo = %d, hi = %d, n_out = %d)", lo, hi, n_out);
     DJV_TRY(check_ptr(z, "z"));
     DJV_TRY(check_idx_ptr(idx, "idx"));
     DJV_TRY(check_idx_ptr(count, "count"));
@@ -683,7 +708,7 @@ djv_status dejavu_select(int B, int n_out, const float* z, djv_mode mode, int k,
     DJV_TRY(check_ws(ws, ws_bytes, sz.off));
     Arena A(ws);
     uint32_t* bits = A.take<uint32_t>((size_t)B * words_of(n_out));
-    SelectJob j{z, n_out, (int)mode, k, mode == DJV_THRESHOLD ? tau_key(t) : 0u, bits, idx, count};
+    SelectJob j{z, n_out, (int)mode, k, mode == DJV_THRESHOLD ? tau_key(t) : 0u, bits, idx, count, lo, hi};
     DJV_HIP(launch_select(&j, 1, B, (hipStream_t)stream, DJV_PROF_SELECT));
     return DJV_OK;
 }
@@ -710,7 +735,7 @@ djv_status dejavu_predict(djv_dtype wt, int B, int d, int r, int n_out, const fl
     DJV_TRY(check_ws(ws, ws_bytes, sz.off));
     Arena A(ws);
     const PredWs w = plan_predict(A, B, d, r, n_out, logits == nullptr, wide);
-    const PredJob j{P1, P2, n_out, (int)mode, k, t, idx, count, logits ? logits : w.z, &w};
+    const PredJob j{P1, P2, n_out, (int)mode, k, t, idx, count, logits ? logits : w.z, &w, 0, n_out};
     return run_predict(wt == DJV_F16, B, d, r, plain_input(y), &j, 1, w.mf, (hipStream_t)stream);
 }
 
@@ -866,7 +891,7 @@ djv_status dejavu_stack_decode(const djv_model* m, const djv_layer* layers, int 
     // input), the second layers run after the attention, and each selection runs in a side
     // block of a later weight stream: S_A^{l+1} beside the MLP up-projection of layer l,
     // S_M^l beside the Q/K/V launch of layer l.
-    const int capA = cap_of(m->mode, m->k_A, m->h, m->B), capM = cap_of(m->mode, m->k_M, m->N, m->B);
+    const int capA = capA_of(*m), capM = capM_of(*m);
     {
         // layer 0's scores from LN(x_0); S_A^0 alone, S_M^0 in layer 0's Q/K/V launch
         const LayerIO io0 = layer_io(x, w, 0, L);

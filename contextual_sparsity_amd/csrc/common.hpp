@@ -254,6 +254,7 @@ struct SelectJob {
     uint32_t* bits;       // [B, words] per-row selection bitmaps (workspace; parallel rows only)
     int32_t* idx;         // [n_out]
     int32_t* count;       // [1]
+    int lo, hi;           // units listed: those in [lo, hi), as j - lo (0, n_out: all)
 };
 
 // One weight matrix served by a GEMV launch (a launch serves up to three, all with rows

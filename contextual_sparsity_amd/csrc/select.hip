@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(SelectJobs jobs, int 
             m1 |= v1[k];
         }
     }
-    const int total = compact_words(m0, m1, J.idx, wtot);
+    const int total = compact_words(m0, m1, J.idx, wtot, J.lo, J.hi);
     if (tid == 0) *J.count = total;
 }
 

@@ -22,7 +22,9 @@
 // off, or heavy ties), and for rows above 49152, the row falls back to a radix select
 // over all keys, reloading them per pass.  Threshold rows are ballots of key > tau.  With one row the block compacts
 // the result into the ascending index list and the device-side count; several rows are
-// ORed (in LDS for a side block, or by a second kernel).
+// ORed (in LDS for a side block, or by a second kernel).  A tensor-parallel shard lists
+// only the kept units of its own range [lo, hi), rebased to its rows (j - lo): the
+// selection itself is over all units, as every shard computes it alike.
 //
 // This header holds the block-level device code; it is used by the selection kernels
 // and by GEMV launches that run a selection in a side block.
@@ -112,18 +114,29 @@ __device__ __forceinline__ void ballot_words(uint32_t* words, int nwords, int j0
     }
 }
 
-// Writes the set bits of words 2t, 2t+1 (t = thread) as ascending indices; returns the
-// total count.
-__device__ __forceinline__ int compact_words(uint32_t m0, uint32_t m1, int32_t* idx, int* wtot) {
+// Bits of word w (indices 32w .. 32w+31) that lie in [lo, hi).
+__device__ __forceinline__ uint32_t range_mask(int w, int lo, int hi) {
+    const int a = lo - 32 * w, b = hi - 32 * w;  // the range inside the word: [a, b)
+    const uint32_t below_b = b >= 32 ? ~0u : (b <= 0 ? 0u : (1u << b) - 1u);
+    const uint32_t from_a = a <= 0 ? ~0u : (a >= 32 ? 0u : ~((1u << a) - 1u));
+    return below_b & from_a;
+}
+
+// Writes the set bits of words 2t, 2t+1 (t = thread) that lie in [lo, hi) as ascending
+// indices j - lo; returns the total count.
+__device__ __forceinline__ int compact_words(uint32_t m0, uint32_t m1, int32_t* idx, int* wtot, int lo,
+                                             int hi) {
     const int w0 = 2 * threadIdx.x, w1 = w0 + 1;
+    m0 &= range_mask(w0, lo, hi);
+    m1 &= range_mask(w1, lo, hi);
     int total;
     int pos = block_exclusive_scan<kThreads>(__popc(m0) + __popc(m1), wtot, &total);
     while (m0) {
-        idx[pos++] = w0 * 32 + (__ffs(m0) - 1);
+        idx[pos++] = w0 * 32 + (__ffs(m0) - 1) - lo;
         m0 &= m0 - 1u;
     }
     while (m1) {
-        idx[pos++] = w1 * 32 + (__ffs(m1) - 1);
+        idx[pos++] = w1 * 32 + (__ffs(m1) - 1) - lo;
         m1 &= m1 - 1u;
     }
     return total;
@@ -202,7 +215,7 @@ __device__ __forceinline__ void finish_row(RowShared& S, const SelectJob& J, int
     if (B == 1) {
         const int w0 = 2 * tid, w1 = 2 * tid + 1;
         const int total = compact_words(w0 < words ? S.selw[w0] : 0u, w1 < words ? S.selw[w1] : 0u,
-                                        J.idx, S.wtot);
+                                        J.idx, S.wtot, J.lo, J.hi);
         if (tid == 0) *J.count = total;
         return;
     }
@@ -533,7 +546,8 @@ __device__ __forceinline__ void select_one_row_block(RowShared& S, const SelectJ
     select_row_full(S, J, 0);
     __syncthreads();
     const int w0 = 2 * tid, w1 = 2 * tid + 1;
-    const int total = compact_words(w0 < words ? S.selw[w0] : 0u, w1 < words ? S.selw[w1] : 0u, J.idx, S.wtot);
+    const int total = compact_words(w0 < words ? S.selw[w0] : 0u, w1 < words ? S.selw[w1] : 0u, J.idx,
+                                    S.wtot, J.lo, J.hi);
     if (tid == 0) *J.count = total;
 }
 
@@ -558,7 +572,8 @@ __device__ __forceinline__ void select_union_block(RowShared& S, const SelectJob
         src = S.uni;
     }
     const int w0 = 2 * tid, w1 = 2 * tid + 1;
-    const int total = compact_words(w0 < words ? src[w0] : 0u, w1 < words ? src[w1] : 0u, J.idx, S.wtot);
+    const int total = compact_words(w0 < words ? src[w0] : 0u, w1 < words ? src[w1] : 0u, J.idx, S.wtot,
+                                    J.lo, J.hi);
     if (tid == 0) *J.count = total;
 }
 
@@ -594,6 +609,7 @@ __device__ __forceinline__ void select_small_block(SmallShared<NT>& S, const Sel
             __syncthreads();
         }
     }
+    sel = sel && tid >= J.lo && tid < J.hi;
     const unsigned long long m = __ballot(sel);
     if (lane == 0) S.wtot[w] = __popcll(m);
     __syncthreads();
@@ -604,7 +620,7 @@ __device__ __forceinline__ void select_small_block(SmallShared<NT>& S, const Sel
         if (q < w) base += t;
         total += t;
     }
-    if (sel) J.idx[base + __popcll(m & ((1ull << lane) - 1ull))] = tid;
+    if (sel) J.idx[base + __popcll(m & ((1ull << lane) - 1ull))] = tid - J.lo;
     if (tid == 0) *J.count = total;
 }
 

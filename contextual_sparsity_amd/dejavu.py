@@ -28,7 +28,7 @@ STATUS_NAMES = {0: "DJV_OK", -1: "DJV_EINVAL", -2: "DJV_EALIGN", -3: "DJV_EWORKS
 # every entry point declared in include/dejavu.h
 EXPORTS = [
     "dejavu_workspace_bytes", "dejavu_workspace_bytes_model", "dejavu_layernorm", "dejavu_select",
-    "dejavu_predict", "dejavu_sparse_mlp", "dejavu_dense_mlp", "dejavu_sparse_mha",
+    "dejavu_select_range", "dejavu_predict", "dejavu_sparse_mlp", "dejavu_dense_mlp", "dejavu_sparse_mha",
     "dejavu_dense_mha", "dejavu_sparse_layer", "dejavu_stack_decode", "dejavu_poll_device_error",
     "dejavu_set_mfma_min_batch", "dejavu_gather_rows", "dejavu_profile_kernel", "dejavu_profile_count",
     "dejavu_last_error", "dejavu_version",
@@ -50,7 +50,8 @@ class djv_model(ctypes.Structure):
                 ("h", ctypes.c_int), ("dh", ctypes.c_int), ("r", ctypes.c_int), ("n", ctypes.c_int),
                 ("n_cap", ctypes.c_int), ("scale", ctypes.c_float), ("eps", ctypes.c_float),
                 ("mode", ctypes.c_int), ("k_A", ctypes.c_int), ("k_M", ctypes.c_int),
-                ("t_A", ctypes.c_float), ("t_M", ctypes.c_float)]
+                ("t_A", ctypes.c_float), ("t_M", ctypes.c_float), ("h_total", ctypes.c_int),
+                ("h_offset", ctypes.c_int), ("N_total", ctypes.c_int), ("N_offset", ctypes.c_int)]
 
 
 class djv_layer(ctypes.Structure):
@@ -80,6 +81,7 @@ def lib() -> ctypes.CDLL:
             "dejavu_workspace_bytes_model": [ctypes.POINTER(djv_model), ctypes.POINTER(_SZ)],
             "dejavu_layernorm": [_I, _I, _P, _P, _F, _P],
             "dejavu_select": [_I, _I, _P, _I, _I, _F, _P, _P, _P, _SZ, _P],
+            "dejavu_select_range": [_I, _I, _P, _I, _I, _F, _I, _I, _P, _P, _P, _SZ, _P],
             "dejavu_predict": [_I, _I, _I, _I, _I, _P, _P, _P, _I, _I, _F, _P, _P, _P, _P, _SZ, _P],
             "dejavu_sparse_mlp": [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _SZ, _P],
             "dejavu_dense_mlp": [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
@@ -187,6 +189,12 @@ def dejavu_select(B, n_out, z, mode, k, t, idx, count, ws, stream=None) -> None:
                                _stream(stream)))
 
 
+def dejavu_select_range(B, n_out, z, mode, k, t, lo, hi, idx, count, ws, stream=None) -> None:
+    wp, wb = _ws(ws)
+    _check(lib().dejavu_select_range(B, n_out, _ptr(z), mode, k, t, lo, hi, _ptr(idx), _ptr(count),
+                                     wp, wb, _stream(stream)))
+
+
 def dejavu_predict(wt, B, d, r, n_out, y, P1, P2, mode, k, t, idx, count, logits, ws,
                    stream=None) -> None:
     wp, wb = _ws(ws)
@@ -225,8 +233,11 @@ def dejavu_dense_mha(wt, B, d, h, dh, n, n_cap, y, Wqkv, Wo, Kc, Vc, scale, resi
 
 
 def make_model(wt, B, d, N, h, dh, r, n, n_cap, scale, mode=DJV_TOPK, k_A=0, k_M=0, t_A=0.5,
-               t_M=0.5, eps=1e-5) -> djv_model:
-    return djv_model(wt, B, d, N, h, dh, r, n, n_cap, scale, eps, mode, k_A, k_M, t_A, t_M)
+               t_M=0.5, eps=1e-5, shard=None) -> djv_model:
+    """shard: None, or (h_total, h_offset, N_total, N_offset) of a tensor-parallel shard
+    whose weights hold h heads and N neurons."""
+    sh = shard or (0, 0, 0, 0)
+    return djv_model(wt, B, d, N, h, dh, r, n, n_cap, scale, eps, mode, k_A, k_M, t_A, t_M, *sh)
 
 
 def make_layer(w: dict, p: Optional[dict] = None) -> djv_layer:

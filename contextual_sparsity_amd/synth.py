@@ -19,7 +19,7 @@ from __future__ import annotations
 
 import math
 from dataclasses import dataclass, replace
-from typing import Dict
+from typing import Dict, Tuple
 
 import torch
 
@@ -123,3 +123,14 @@ def make_scores(B: int, n_out: int, seed: int, device="cpu", alphabet=None) -> t
     a = torch.tensor(alphabet, dtype=torch.float32)
     idx = torch.randint(0, len(alphabet), (B, n_out), generator=g)
     return a[idx].to(device)
+
+
+def shard_layer(w: Dict[str, torch.Tensor], heads: Tuple[int, int], neurons: Tuple[int, int],
+                dh: int) -> Dict[str, torch.Tensor]:
+    """One tensor-parallel shard of a layer: the Wqkv blocks, Wo rows and caches of heads
+    [lo, hi) and the W1, b1, W2 rows of neurons [lo, hi), as contiguous copies."""
+    (h0, h1), (n0, n1) = heads, neurons
+    return {"Wqkv": w["Wqkv"][h0:h1].contiguous(), "Wo": w["Wo"][h0 * dh:h1 * dh].contiguous(),
+            "W1": w["W1"][n0:n1].contiguous(), "b1": w["b1"][n0:n1].contiguous(),
+            "W2": w["W2"][n0:n1].contiguous(), "K": w["K"][:, h0:h1].contiguous(),
+            "V": w["V"][:, h0:h1].contiguous()}

@@ -108,6 +108,16 @@ djv_status dejavu_select(int B, int n_out, const float* z, djv_mode mode, int k,
                          int32_t* idx, int32_t* count, void* ws, size_t ws_bytes, void* stream);
 
 /* --------------------------------------------------------------------------------------
+ * dejavu_select_range -- dejavu_select over all n_out units, listing only the kept units j
+ *   with lo <= j < hi, as j - lo (a tensor-parallel shard's part of the set, in its own
+ *   row numbering; see djv_model's shard fields).  idx has room for hi - lo entries.
+ *   0 <= lo <= hi <= n_out (DJV_EINVAL otherwise); the workspace is dejavu_select's.
+ * ------------------------------------------------------------------------------------ */
+djv_status dejavu_select_range(int B, int n_out, const float* z, djv_mode mode, int k, float t,
+                               int lo, int hi, int32_t* idx, int32_t* count, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/* --------------------------------------------------------------------------------------
  * dejavu_predict -- sparsity predictor and selection: z = P2 . ReLU(P1 . y[b]) for each b
  *   (fp32 accumulation, scores stored fp32), then dejavu_select(z).
  *   [BLOG section 2]: a two-layer MLP per block type whose output width is the number of
@@ -200,11 +210,23 @@ typedef struct djv_model {
     djv_mode mode;           /* selection rule for both predictors */
     int k_A, k_M;            /* top-k sizes (DJV_TOPK) */
     float t_A, t_M;          /* thresholds (DJV_THRESHOLD) */
+    /* Tensor-parallel shard (all four 0: unsharded).  The blocks' sums run over heads and
+     * neurons ([NOTES "Sparsified MLP"], [NOTES "Sparsified Attention"]), so g GPUs can each
+     * hold a contiguous range of them and add their parts.  h_total > 0: the head
+     * predictor scores all h_total heads (P2_A [h_total, r]) and selects among them (k_A
+     * counts over all), and this model's Wqkv, Wo, Kc, Vc hold the h heads from h_offset;
+     * its head list holds the kept heads of that range, as head - h_offset.  N_total,
+     * N_offset: the same for the neurons (P2_M [N_total, r]; W1, b1, W2 hold the N
+     * neurons from N_offset).  Each block then adds the shard's part of its sum to x; the
+     * sum of the parts over shards (an all-reduce between blocks, not made here) is the
+     * unsharded block.  Traces: z_A [L, B, h_total], z_M [L, B, N_total], sets local. */
+    int h_total, h_offset, N_total, N_offset;
 } djv_model;
 
 /* Optional per-layer trace for tests (device pointers, each may be NULL):
  *   x_in [L, B, d]: each layer's input x; x_mid [L, B, d]: each layer's x' (after
- *   attention); z_A [L, B, h] / z_M [L, B, N]: the predictor scores the layer's sets were
+ *   attention); z_A [L, B, h] / z_M [L, B, N] (h_total / N_total for a shard): the
+ *   predictor scores the layer's sets were
  *   selected from; sets_A [L, h] / sets_M [L, N]: the selected index lists (first
  *   counts[l, 0] / counts[l, 1] entries valid); counts [L, 2]. */
 typedef struct djv_trace {

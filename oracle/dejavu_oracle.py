@@ -328,6 +328,41 @@ def dense_layer(x, L: LayerWeights, n: int, scale: float):
     return x2, x1
 
 
+# --------------------------------------------------------------------------------------
+# Tensor-parallel shards  [NOTES "Sparsified MLP"], [NOTES "Sparsified Attention"]
+# --------------------------------------------------------------------------------------
+def shard_set(S, lo: int, hi: int) -> np.ndarray:
+    """The part of a selected set that falls in a shard's unit range [lo, hi), renumbered
+    from the shard's first unit: {j - lo : j in S, lo <= j < hi}, ascending.
+
+    Both sparse blocks are sums over the kept units (MLP_{S_M} over neurons, MHA_{S_A}
+    over heads), so a shard holding a contiguous range of units computes the terms of its
+    own kept units; the pages do not discuss several GPUs, this is that sum split by
+    ranges.  Every shard selects from the same global scores.
+    """
+    S = np.asarray(S, dtype=np.int64)
+    return (S[(S >= lo) & (S < hi)] - lo).astype(np.int32)
+
+
+def shard_ranges(n: int, g: int) -> list:
+    """g contiguous ranges covering 0..n-1, the first n % g one unit longer."""
+    base, extra = divmod(n, g)
+    out, lo = [], 0
+    for i in range(g):
+        hi = lo + base + (1 if i < extra else 0)
+        out.append((lo, hi))
+        lo = hi
+    return out
+
+
+def shard_layer_weights(L: "LayerWeights", h_lo: int, h_hi: int, n_lo: int, n_hi: int, dh: int):
+    """The rows of one shard: heads h_lo..h_hi-1 (their Wqkv blocks, Wo rows and caches)
+    and neurons n_lo..n_hi-1 (W1, b1, W2 rows)."""
+    return LayerWeights(Wqkv=L.Wqkv[h_lo:h_hi], Wo=L.Wo[h_lo * dh:h_hi * dh], W1=L.W1[n_lo:n_hi],
+                        b1=L.b1[n_lo:n_hi], W2=L.W2[n_lo:n_hi], K=L.K[:, h_lo:h_hi],
+                        V=L.V[:, h_lo:h_hi])
+
+
 @dataclass
 class Selection:
     """Selection rule shared by both predictors of a layer."""

@@ -25,15 +25,29 @@ class Stack:
     """Seeded weights of L layers on the device plus the library descriptors."""
 
     def __init__(self, shape: synth.LayerShape, L: int, seed: int, k_A: int, k_M: int,
-                 mode=dj.DJV_TOPK, t_A=0.5, t_M=0.5):
-        self.s, self.L = shape, L
-        self.w = [synth.make_layer(shape, seed, l, DEV) for l in range(L)]
+                 mode=dj.DJV_TOPK, t_A=0.5, t_M=0.5, shard=None):
+        """shard = (g, i): shard i of g of a tensor-parallel split of `shape`'s heads and
+        neurons (full predictors, the shard's slices of the full layer weights)."""
+        self.full, self.L = shape, L
+        if shard is None:
+            self.hr, self.nr, sh = (0, shape.h), (0, shape.N), None
+            self.s = shape
+            self.w = [synth.make_layer(shape, seed, l, DEV) for l in range(L)]
+        else:
+            g, i = shard
+            self.hr, self.nr = configs.shard_range(shape.h, g, i), configs.shard_range(shape.N, g, i)
+            sh = (shape.h, self.hr[0], shape.N, self.nr[0])
+            self.s = shape.with_(h=self.hr[1] - self.hr[0], N=self.nr[1] - self.nr[0])
+            self.w = [synth.shard_layer(synth.make_layer(shape, seed, l, DEV), self.hr, self.nr, shape.dh)
+                      for l in range(L)]
+        self.sharded = shard is not None
         self.p = [synth.make_predictors(shape, seed, l, DEV) for l in range(L)]
         self.x0 = synth.make_input(shape, seed, DEV)
         self.k_A, self.k_M, self.mode, self.t_A, self.t_M = k_A, k_M, mode, t_A, t_M
         self.scale = shape.dh ** -0.5
-        self.m = dj.make_model(wt_code(shape), shape.B, shape.d, shape.N, shape.h, shape.dh, shape.r,
-                               shape.n, shape.cap, self.scale, mode, k_A, k_M, t_A, t_M)
+        s = self.s
+        self.m = dj.make_model(wt_code(s), s.B, s.d, s.N, s.h, s.dh, s.r, s.n, s.cap, self.scale, mode,
+                               k_A, k_M, t_A, t_M, shard=sh)
         self.desc = [dj.make_layer(self.w[l], self.p[l]) for l in range(L)]
         self.ws = dj.workspace(dj.dejavu_workspace_bytes_model(self.m), DEV)
         # host copies of the caches before the step (the step appends at position n)
@@ -44,7 +58,8 @@ class Stack:
         s, L = self.s, self.L
         f = lambda *shape: torch.zeros(*shape, dtype=torch.float32, device=DEV)
         i = lambda *shape: torch.full(shape, -1, dtype=torch.int32, device=DEV)
-        t = dict(x_in=f(L, s.B, s.d), x_mid=f(L, s.B, s.d), z_A=f(L, s.B, s.h), z_M=f(L, s.B, s.N),
+        t = dict(x_in=f(L, s.B, s.d), x_mid=f(L, s.B, s.d), z_A=f(L, s.B, self.full.h),
+                 z_M=f(L, s.B, self.full.N),
                  sets_A=i(L, s.h), sets_M=i(L, s.N), counts=i(L, 2))
         return t, dj.make_trace(**t)
 
@@ -83,10 +98,10 @@ def check_stack(st: Stack, x_out, tr, lookahead: bool, sel_k=True):
         zA_ref = O.predictor_logits_f64(O.layernorm(src_A), host(p["P1_A"]), host(p["P2_A"]))
         zM_ref = O.predictor_logits_f64(O.layernorm(src_M), host(p["P1_M"]), host(p["P2_M"]))
         assert rel_l2(zA, zA_ref) < tol and rel_l2(zM, zM_ref) < tol, l
-        # bit-exact selection on the GPU's own scores
-        assert np.array_equal(S_A, O.select(zA, st.mode, st.k_A, st.t_A)), l
-        assert np.array_equal(S_M, O.select(zM, st.mode, st.k_M, st.t_M)), l
-        if st.mode == dj.DJV_TOPK and s.B == 1:
+        # bit-exact selection on the GPU's own scores (a shard lists its part of the set)
+        assert np.array_equal(S_A, O.shard_set(O.select(zA, st.mode, st.k_A, st.t_A), *st.hr)), l
+        assert np.array_equal(S_M, O.shard_set(O.select(zM, st.mode, st.k_M, st.t_M), *st.nr)), l
+        if st.mode == dj.DJV_TOPK and s.B == 1 and not st.sharded:
             check_sets_valid(S_A, zA_ref[0], st.k_A, float(np.abs(zA[0] - zA_ref[0]).max()))
             check_sets_valid(S_M, zM_ref[0], st.k_M, float(np.abs(zM[0] - zM_ref[0]).max()))
         # attention half from the GPU's input and head set

@@ -371,3 +371,57 @@ def test_lookahead_schedule():
         assert sets[l][0].tolist() == S_A.tolist() and sets[l][1].tolist() == S_M.tolist()
         assert _rel(xs[l + 1], O.sparse_layer(xs[l], layers[l], *sets[l], 7, 0.4)[0]) < 1e-15
     assert xL is xs[-1]
+
+
+# ------------------------------------------------------------------------------ shards
+@pytest.mark.parametrize("n,g", [(10, 3), (96, 8), (7, 7), (5, 1), (33, 4), (49152, 8)])
+def test_shard_ranges_partition(n, g):
+    R = O.shard_ranges(n, g)
+    assert len(R) == g and R[0][0] == 0 and R[-1][1] == n
+    assert all(a[1] == b[0] for a, b in zip(R, R[1:]))
+    sizes = [hi - lo for lo, hi in R]
+    assert max(sizes) - min(sizes) <= 1 and sizes == sorted(sizes, reverse=True)
+
+
+def test_shard_set_brute_force():
+    S = [0, 3, 4, 9]
+    assert O.shard_set(S, 3, 9).tolist() == [0, 1]
+    assert O.shard_set(S, 9, 10).tolist() == [0]
+    assert O.shard_set(S, 0, 3).tolist() == [0]
+    assert O.shard_set(S, 5, 5).tolist() == []
+    assert O.shard_set([], 0, 4).tolist() == []
+
+
+def test_shard_sets_partition_the_global_set():
+    rng = np.random.default_rng(5)
+    for n in (1, 31, 32, 33, 100):
+        for g in (1, 2, 3, 7):
+            if g > n:
+                continue
+            S = np.sort(rng.choice(n, size=int(rng.integers(0, n + 1)), replace=False)).astype(np.int32)
+            parts = []
+            for lo, hi in O.shard_ranges(n, g):
+                p = O.shard_set(S, lo, hi)
+                assert p.dtype == np.int32 and (np.diff(p) > 0).all()
+                assert ((p >= 0) & (p < hi - lo)).all()
+                parts.append(p + lo)
+            assert np.array_equal(np.concatenate(parts), S), (n, g)
+
+
+@pytest.mark.parametrize("g", [1, 2, 3, 4])
+def test_shard_blocks_sum_to_the_unsharded_blocks(g):
+    s, L, P, x = _tiny(B=2)
+    y = O.layernorm(x)
+    S_A, S_M = np.array([0, 2, 3]), np.array([1, 5, 6, 17, 22, 30, 39])
+    att, kn, vn = O.sparse_mha(y, L.Wqkv, L.Wo, L.K, L.V, s.n, S_A, 0.5)
+    mlp = O.sparse_mlp(y, L.W1, L.b1, L.W2, S_M)
+    att_sum, mlp_sum, kn_parts = np.zeros_like(att), np.zeros_like(mlp), []
+    for (hlo, hhi), (nlo, nhi) in zip(O.shard_ranges(s.h, g), O.shard_ranges(s.N, g)):
+        Ls = O.shard_layer_weights(L, hlo, hhi, nlo, nhi, s.dh)
+        a, k_s, _ = O.sparse_mha(y, Ls.Wqkv, Ls.Wo, Ls.K, Ls.V, s.n, O.shard_set(S_A, hlo, hhi), 0.5)
+        att_sum += a
+        kn_parts.append(k_s)
+        mlp_sum += O.sparse_mlp(y, Ls.W1, Ls.b1, Ls.W2, O.shard_set(S_M, nlo, nhi))
+    assert _rel(att_sum, att) < 1e-13 and _rel(mlp_sum, mlp) < 1e-13
+    # the shards' new K rows, in shard order, are the unsharded call's rows
+    assert np.array_equal(np.concatenate(kn_parts, axis=1), kn)

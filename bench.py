@@ -83,6 +83,10 @@ def parse(argv=None):
     ap.add_argument("--threshold", action="store_true",
                     help="threshold-mode selection: t calibrated on layer 0's scores to the keep "
                          "percentages; one JSON line with the kept-count spread")
+    ap.add_argument("--tp", type=int, default=1,
+                    help="time one tensor-parallel shard of the workload split over this many GPUs "
+                         "(full predictors, the shard's heads and neurons); one JSON line")
+    ap.add_argument("--tp-rank", type=int, default=0, help="which shard --tp times")
     ap.add_argument("--ablation", action="store_true",
                     help="the fusion ablation: fused sparse MLP vs gather-then-dense, OPT-175B shape")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -342,12 +346,26 @@ def main(argv=None) -> int:
     k_A, k_M = wl.k_A, wl.k_M
     dev = "cuda"
     log(f"{dj.dejavu_version()}  device {torch.cuda.get_device_name(0)}  workload {wl.name} L={L}")
+    # a tensor-parallel shard: the predictors (and the selection) stay whole, the layer
+    # weights and caches are the shard's heads and neurons
+    if not (1 <= args.tp <= s.h and 0 <= args.tp_rank < args.tp):
+        print(f"--tp {args.tp} --tp-rank {args.tp_rank}: need 1 <= tp <= h and 0 <= rank < tp",
+              file=sys.stderr)
+        return 2
+    shard = None
+    s_loc = s
+    if args.tp > 1:
+        hr = configs.shard_range(s.h, args.tp, args.tp_rank)
+        nr = configs.shard_range(s.N, args.tp, args.tp_rank)
+        s_loc = s.with_(h=hr[1] - hr[0], N=nr[1] - nr[0])
+        shard = (s.h, hr[0], s.N, nr[0])
+        log(f"shard {args.tp_rank} of {args.tp}: heads {hr}, neurons {nr}")
 
     # ---- seeded weights, all resident before timing
     t0 = time.time()
     layers, preds = [], []
     for l in range(L):
-        layers.append(synth.make_layer(s, args.seed, l, dev))
+        layers.append(synth.make_layer(s_loc, args.seed, l, dev))
         preds.append(synth.make_predictors(s, args.seed, l, dev))
         if l % 4 == 3 or l == L - 1:
             torch.cuda.synchronize()
@@ -355,7 +373,9 @@ def main(argv=None) -> int:
                 f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB)")
     x0 = synth.make_input(s, args.seed, dev)
     wt = dj.DJV_F16 if s.dtype == "f16" else dj.DJV_F32
-    m = dj.make_model(wt, s.B, s.d, s.N, s.h, s.dh, s.r, s.n, s.cap, wl.scale, dj.DJV_TOPK, k_A, k_M)
+    sl = s_loc
+    m = dj.make_model(wt, s.B, s.d, sl.N, sl.h, s.dh, s.r, s.n, s.cap, wl.scale, dj.DJV_TOPK, k_A, k_M,
+                      shard=shard)
     thr = None
     if args.threshold:
         # t_A, t_M: sigmoid of the score quantiles that keep pct_A / pct_M of layer 0's units
@@ -374,8 +394,8 @@ def main(argv=None) -> int:
             dj.dejavu_predict(wt, s.B, s.d, s.r, n_out, xn, P1, P2, dj.DJV_TOPK, 1, 0.5, idx, cnt, z, pws)
             q = torch.quantile(z.flatten().double().cpu(), 1.0 - pct / 100.0).item()
             ts.append(float(torch.sigmoid(torch.tensor(q)).item()))
-        m = dj.make_model(wt, s.B, s.d, s.N, s.h, s.dh, s.r, s.n, s.cap, wl.scale, dj.DJV_THRESHOLD, 0, 0,
-                          t_A=ts[0], t_M=ts[1])
+        m = dj.make_model(wt, s.B, s.d, sl.N, sl.h, s.dh, s.r, s.n, s.cap, wl.scale, dj.DJV_THRESHOLD, 0,
+                          0, t_A=ts[0], t_M=ts[1], shard=shard)
         thr = {"t_A": ts[0], "t_M": ts[1]}
     desc = [dj.make_layer(layers[l], preds[l]) for l in range(L)]
     ws = dj.workspace(dj.dejavu_workspace_bytes_model(m), dev)
@@ -418,25 +438,32 @@ def main(argv=None) -> int:
         d = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(used)]
         return sum(d) / max(1, len(d)), used
 
-    if thr is not None:
+    if thr is not None or shard is not None:
+        # kept counts vary by layer: bytes from each layer's own counts
         counts = torch.zeros(L, 2, dtype=torch.int32, device=dev)
         x.copy_(x0)
         dj.dejavu_stack_decode(m, desc, x, lookahead, False, dj.make_trace(counts=counts), ws, s_main)
         c = counts.cpu().double()
         e = 2 if s.dtype == "f16" else 4
-        lbs = [(2 * s.d * s.r + s.r * s.N + s.r * s.h) * e + 4 * s.d * s.dh * int(c[l, 0]) * e
-               + s.B * 2 * (s.n + 1) * s.dh * int(c[l, 0]) * e + (2 * s.d + 1) * int(c[l, 1]) * e for l in range(L)]
+        pred_b = (2 * s.d * s.r + s.r * s.N + s.r * s.h) * e  # whole predictors, on every shard
+        lbs = [pred_b + 4 * s.d * s.dh * int(c[l, 0]) * e + s.B * 2 * (s.n + 1) * s.dh * int(c[l, 0]) * e
+               + (2 * s.d + 1) * int(c[l, 1]) * e for l in range(L)]
         step_bytes_t = sum(lbs)
-        out = {"mode": "threshold", "workload": wl.name, "layers": L, "t_A": round(thr["t_A"], 6),
-               "t_M": round(thr["t_M"], 6), "ms_per_step": round(ms_step, 4),
-               "us_per_layer": round(ms_step * 1e3 / L, 2),
-               "GBps": round(step_bytes_t / (ms_step * 1e-3) / 1e9, 1),
-               "pct_of_peak": round(100 * step_bytes_t / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
-               "kept_heads": {"mean": round(c[:, 0].mean().item(), 2), "min": int(c[:, 0].min()),
-                              "max": int(c[:, 0].max())},
-               "kept_neurons": {"mean": round(c[:, 1].mean().item(), 1), "min": int(c[:, 1].min()),
-                                "max": int(c[:, 1].max())},
-               "bytes_per_layer_mean": round(step_bytes_t / L)}
+        out = {"mode": "threshold" if thr else "top-k", "workload": wl.name, "layers": L}
+        if thr:
+            out.update({"t_A": round(thr["t_A"], 6), "t_M": round(thr["t_M"], 6)})
+        if shard:
+            out.update({"tp": args.tp, "tp_rank": args.tp_rank, "shard_heads": sl.h, "shard_neurons": sl.N,
+                        "predictor_share_of_bytes": round(pred_b * L / step_bytes_t, 3)})
+        out.update({"ms_per_step": round(ms_step, 4),
+                    "us_per_layer": round(ms_step * 1e3 / L, 2),
+                    "GBps": round(step_bytes_t / (ms_step * 1e-3) / 1e9, 1),
+                    "pct_of_peak": round(100 * step_bytes_t / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                    "kept_heads": {"mean": round(c[:, 0].mean().item(), 2), "min": int(c[:, 0].min()),
+                                   "max": int(c[:, 0].max())},
+                    "kept_neurons": {"mean": round(c[:, 1].mean().item(), 1), "min": int(c[:, 1].min()),
+                                     "max": int(c[:, 1].max())},
+                    "bytes_per_layer_mean": round(step_bytes_t / L)})
         if args.breakdown:
             out["kernels_us"] = {fam: round(family_time(fam, max(3, args.steps // 4))[0] * 1e3, 2)
                                  for fam in ("qkv", "mlp_up", "mlp_down", "o_proj", "attn", "pred_1",

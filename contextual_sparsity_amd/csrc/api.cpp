@@ -24,6 +24,8 @@ namespace djv {
 // ablation); row_bytes a multiple of 2.
 hipError_t launch_gather_rows(const void* W, void* out, const UnitList& list, int rpu, size_t row_bytes,
                               unsigned* flags, hipStream_t s);
+// norms.hip: scores[u] = sqrt(sum over b and c of v[b, u, c]^2), v [B, units, w] fp32.
+hipError_t launch_unit_norms(const float* v, int B, int units, int w, float* scores, hipStream_t s);
 }  // namespace djv
 
 namespace {
@@ -833,6 +835,74 @@ djv_status dejavu_dense_mha(djv_dtype wt, int B, int d, int h, int dh, int n, in
                             size_t ws_bytes, void* stream) {
     return mha_common(wt, B, d, h, dh, n, n_cap, y, Wqkv, Wo, Kc, Vc, nullptr, nullptr, h, scale,
                       resid, out, ws, ws_bytes, stream);
+}
+
+// ------------------------------------------------------------------------------------
+// Output norms: the scores of the "true" selection
+// ------------------------------------------------------------------------------------
+djv_status dejavu_neuron_norms(djv_dtype wt, int B, int d, int N, const float* y, const void* W1,
+                               const void* b1, float* scores, void* ws, size_t ws_bytes,
+                               void* stream) {
+    DJV_TRY(check_dtype(wt));
+    DJV_TRY(check_batch(B));
+    DJV_TRY(check_rowlen(d, wt, "d"));
+    DJV_TRY(check_wide_batch(B, wt, {d}));
+    DJV_REQUIRE(N >= 1, DJV_EINVAL, "N must be >= 1");
+    DJV_TRY(check_ptr(y, "y"));
+    DJV_TRY(check_ptr(W1, "W1"));
+    DJV_REQUIRE(b1 != nullptr, DJV_EINVAL, "b1 is NULL");
+    DJV_TRY(check_ptr(scores, "scores"));
+    const bool f16 = wt == DJV_F16;
+    Arena sz(nullptr);
+    const bool wide = wide_possible(wt, {d});
+    plan_mlp(sz, B, d, N, f16, wide);
+    DJV_TRY(check_ws(ws, ws_bytes, sz.off));
+    Arena A(ws);
+    const MlpWs w = plan_mlp(A, B, d, N, f16, wide);
+    const hipStream_t s = (hipStream_t)stream;
+    // the dense up-projection's activations a [B, N], then their norms across the batch
+    GemvArgs g = gemv_args(d, B, DJV_PROF_MLP_UP, w.mf);
+    add_seg(g, seg_up(W1, b1, UnitList{nullptr, nullptr, N, N}, plain_input(y), w.a));
+    DJV_HIP(launch_gemv(f16, g, s));
+    DJV_HIP(launch_unit_norms(w.a, B, N, 1, scores, s));
+    return DJV_OK;
+}
+
+djv_status dejavu_head_norms(djv_dtype wt, int B, int d, int h, int dh, int n, int n_cap,
+                             const float* y, const void* Wqkv, void* Kc, void* Vc, float scale,
+                             float* scores, void* ws, size_t ws_bytes, void* stream) {
+    DJV_TRY(check_dtype(wt));
+    DJV_TRY(check_batch(B));
+    DJV_TRY(check_rowlen(d, wt, "d"));
+    DJV_TRY(check_wide_batch(B, wt, {d}));
+    DJV_REQUIRE(h >= 1, DJV_EINVAL, "h must be >= 1");
+    DJV_REQUIRE(dh == 64 || dh == 128, DJV_EUNSUPPORTED, "dh must be 64 or 128 (got %d)", dh);
+    DJV_REQUIRE(n >= 0 && n < n_cap, DJV_EINVAL, "need 0 <= n < n_cap (n = %d, n_cap = %d)", n, n_cap);
+    DJV_REQUIRE((n_cap + attn_chunk_for(wt == DJV_F16, dh) - 1) / attn_chunk_for(wt == DJV_F16, dh)
+                    <= kAttnMaxChunks, DJV_EUNSUPPORTED, "n_cap = %d is too long", n_cap);
+    DJV_REQUIRE(std::isfinite(scale), DJV_EINVAL, "scale must be finite");
+    DJV_TRY(check_ptr(y, "y"));
+    DJV_TRY(check_ptr(Wqkv, "Wqkv"));
+    DJV_TRY(check_ptr(Kc, "Kc"));
+    DJV_TRY(check_ptr(Vc, "Vc"));
+    DJV_TRY(check_ptr(scores, "scores"));
+    const bool f16 = wt == DJV_F16;
+    Arena sz(nullptr);
+    const bool wide = wide_possible(wt, {d});
+    plan_mha(sz, B, d, dh, h, n_cap, f16, wide);
+    DJV_TRY(check_ws(ws, ws_bytes, sz.off));
+    Arena A(ws);
+    const MhaWs w = plan_mha(A, B, d, dh, h, n_cap, f16, wide);
+    const hipStream_t s = (hipStream_t)stream;
+    // Q/K/V of every head (K/V appended at n), attention merged into H [B, h, dh], norms
+    const UnitList heads{nullptr, nullptr, h, h};
+    GemvArgs g = gemv_args(d, B, DJV_PROF_QKV, w.mf);
+    g.Kc = Kc; g.Vc = Vc; g.h = h; g.dh = dh; g.n = n; g.n_cap = n_cap;
+    add_seg(g, seg_qkv(Wqkv, heads, dh, plain_input(y), w.q));
+    DJV_HIP(launch_gemv(f16, g, s));
+    DJV_HIP(launch_attention(f16, attend_args(B, h, dh, n, n_cap, Kc, Vc, heads, scale, w), true, s));
+    DJV_HIP(launch_unit_norms(w.H, B, h, dh, scores, s));
+    return DJV_OK;
 }
 
 djv_status dejavu_sparse_layer(const djv_model* m, const djv_layer* layer, float* x,

@@ -28,8 +28,9 @@ STATUS_NAMES = {0: "DJV_OK", -1: "DJV_EINVAL", -2: "DJV_EALIGN", -3: "DJV_EWORKS
 # every entry point declared in include/dejavu.h
 EXPORTS = [
     "dejavu_workspace_bytes", "dejavu_workspace_bytes_model", "dejavu_layernorm", "dejavu_select",
-    "dejavu_select_range", "dejavu_predict", "dejavu_sparse_mlp", "dejavu_dense_mlp", "dejavu_sparse_mha",
-    "dejavu_dense_mha", "dejavu_sparse_layer", "dejavu_stack_decode", "dejavu_poll_device_error",
+    "dejavu_select_range", "dejavu_predict", "dejavu_sparse_mlp", "dejavu_dense_mlp",
+    "dejavu_sparse_mha", "dejavu_dense_mha", "dejavu_neuron_norms", "dejavu_head_norms",
+    "dejavu_sparse_layer", "dejavu_stack_decode", "dejavu_poll_device_error",
     "dejavu_set_mfma_min_batch", "dejavu_gather_rows", "dejavu_profile_kernel", "dejavu_profile_count",
     "dejavu_last_error", "dejavu_version",
 ]
@@ -82,6 +83,8 @@ def lib() -> ctypes.CDLL:
             "dejavu_layernorm": [_I, _I, _P, _P, _F, _P],
             "dejavu_select": [_I, _I, _P, _I, _I, _F, _P, _P, _P, _SZ, _P],
             "dejavu_select_range": [_I, _I, _P, _I, _I, _F, _I, _I, _P, _P, _P, _SZ, _P],
+            "dejavu_neuron_norms": [_I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P],
+            "dejavu_head_norms": [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _F, _P, _P, _SZ, _P],
             "dejavu_predict": [_I, _I, _I, _I, _I, _P, _P, _P, _I, _I, _F, _P, _P, _P, _P, _SZ, _P],
             "dejavu_sparse_mlp": [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _SZ, _P],
             "dejavu_dense_mlp": [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
@@ -193,6 +196,18 @@ def dejavu_select_range(B, n_out, z, mode, k, t, lo, hi, idx, count, ws, stream=
     wp, wb = _ws(ws)
     _check(lib().dejavu_select_range(B, n_out, _ptr(z), mode, k, t, lo, hi, _ptr(idx), _ptr(count),
                                      wp, wb, _stream(stream)))
+
+
+def dejavu_neuron_norms(wt, B, d, N, y, W1, b1, scores, ws, stream=None) -> None:
+    wp, wb = _ws(ws)
+    _check(lib().dejavu_neuron_norms(wt, B, d, N, _ptr(y), _ptr(W1), _ptr(b1), _ptr(scores), wp, wb,
+                                     _stream(stream)))
+
+
+def dejavu_head_norms(wt, B, d, h, dh, n, n_cap, y, Wqkv, Kc, Vc, scale, scores, ws, stream=None) -> None:
+    wp, wb = _ws(ws)
+    _check(lib().dejavu_head_norms(wt, B, d, h, dh, n, n_cap, _ptr(y), _ptr(Wqkv), _ptr(Kc), _ptr(Vc),
+                                   scale, _ptr(scores), wp, wb, _stream(stream)))
 
 
 def dejavu_predict(wt, B, d, r, n_out, y, P1, P2, mode, k, t, idx, count, logits, ws,

@@ -191,6 +191,31 @@ djv_status dejavu_dense_mha(djv_dtype wt, int B, int d, int h, int dh, int n, in
                             void* ws, size_t ws_bytes, void* stream);
 
 /* --------------------------------------------------------------------------------------
+ * dejavu_neuron_norms -- the neuron scores of the "true" selection: scores[j] =
+ *   sqrt(sum_b a[b, j]^2) with a[b, j] = ReLU(W1[j] . y[b] + b1[j]), for all N neurons.
+ *   [BLOG section 1 "Contextual Sparsity"]: a dense pass records each neuron's activations
+ *   across the tokens and ranks the neurons by the L2 norm of that row; the tokens here
+ *   are the B batch rows.  Dense: reads all of W1.  scores [N] fp32 (device).  Select on
+ *   them with dejavu_select (one row) to get the true set.
+ * ------------------------------------------------------------------------------------ */
+djv_status dejavu_neuron_norms(djv_dtype wt, int B, int d, int N, const float* y,
+                               const void* W1, const void* b1, float* scores,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/* --------------------------------------------------------------------------------------
+ * dejavu_head_norms -- the head scores of the "true" selection: scores[i] =
+ *   sqrt(sum_b ||H_i(y[b])||^2), H_i(y[b]) the head's attention output (d_h values, before
+ *   the output projection) over positions 0..n as in dejavu_dense_mha, for all h heads.
+ *   [BLOG section 1 "Contextual Sparsity"]: each head's output is a matrix (tokens x d_h)
+ *   and the heads are ranked by its L2 norm.  Like dejavu_dense_mha it computes every
+ *   head's K/V of y and writes them at position n of Kc / Vc.  scores [h] fp32 (device).
+ *   Workspace: dejavu_workspace_bytes with these B, d, h, dh, n_cap.
+ * ------------------------------------------------------------------------------------ */
+djv_status dejavu_head_norms(djv_dtype wt, int B, int d, int h, int dh, int n, int n_cap,
+                             const float* y, const void* Wqkv, void* Kc, void* Vc, float scale,
+                             float* scores, void* ws, size_t ws_bytes, void* stream);
+
+/* --------------------------------------------------------------------------------------
  * Layer and stack descriptors (host structs holding device pointers).
  * ------------------------------------------------------------------------------------ */
 typedef struct djv_layer {

@@ -281,6 +281,55 @@ def dense_mha(y, Wqkv, Wo, K, V, n: int, scale: float):
 
 
 # --------------------------------------------------------------------------------------
+# "True" selection by output norm  [BLOG §1 "Contextual Sparsity"]
+# --------------------------------------------------------------------------------------
+def neuron_norms(y, W1, b1) -> np.ndarray:
+    """Per-neuron score: the L2 norm of the neuron's activations across the tokens.
+
+    [BLOG §1]: for the MLP the norm is not taken of a token's output vector; the MLP acts
+    per position, so its hidden activations form a (neurons x tokens) matrix and each
+    neuron is scored by the norm of its row.  The tokens of one decode step are the batch
+    rows of y.  Returns [N] float64.
+    """
+    y = _f64(y)
+    a = np.maximum(0.0, y @ _f64(W1).T + _f64(b1)[None, :])  # [B, N]
+    return np.sqrt((a * a).sum(axis=0))
+
+
+def head_norms(y, Wqkv, K, V, n: int, scale: float) -> np.ndarray:
+    """Per-head score: the L2 (Frobenius) norm of the head's output matrix over the tokens.
+
+    [BLOG §1]: each head's output is a matrix (tokens x d_h, the head's slice of the
+    attention output before the output projection), scored by its L2 norm.  H_i is the
+    head's attention over positions 0..n with its own K/V of y appended at position n
+    (rounded to the cache dtype), as in ``sparse_mha``.  Returns [h] float64.
+    """
+    y = _f64(y)
+    B = y.shape[0]
+    h = Wqkv.shape[0]
+    sq = np.zeros(h)
+    for i in range(h):
+        for b in range(B):
+            q = _f64(Wqkv[i, 0]) @ y[b]
+            k = _round_to(_f64(Wqkv[i, 1]) @ y[b], K.dtype)
+            v = _round_to(_f64(Wqkv[i, 2]) @ y[b], V.dtype)
+            keys = np.concatenate([_f64(K[b, i, :n]), _f64(k)[None, :]])
+            vals = np.concatenate([_f64(V[b, i, :n]), _f64(v)[None, :]])
+            H = _attend(q, keys, vals, scale)
+            sq[i] += float(H @ H)
+    return np.sqrt(sq)
+
+
+def recall(S_pred, S_true) -> float:
+    """Share of the true set that the predicted set holds: |S_pred & S_true| / |S_true|
+    (1.0 for an empty true set)."""
+    t = set(int(j) for j in S_true)
+    if not t:
+        return 1.0
+    return len(t & set(int(j) for j in S_pred)) / len(t)
+
+
+# --------------------------------------------------------------------------------------
 # Layer and stack
 # --------------------------------------------------------------------------------------
 @dataclass

@@ -425,3 +425,58 @@ def test_shard_blocks_sum_to_the_unsharded_blocks(g):
     assert _rel(att_sum, att) < 1e-13 and _rel(mlp_sum, mlp) < 1e-13
     # the shards' new K rows, in shard order, are the unsharded call's rows
     assert np.array_equal(np.concatenate(kn_parts, axis=1), kn)
+
+
+# ------------------------------------------------------------------------------ output norms
+def test_neuron_norms_single_token_is_the_activation():
+    s, L, P, x = _tiny(B=1)
+    y = O.layernorm(x)
+    a = np.maximum(0.0, y @ np.asarray(L.W1, np.float64).T + np.asarray(L.b1, np.float64))[0]
+    assert _rel(O.neuron_norms(y, L.W1, L.b1), a) < 1e-15
+
+
+def test_neuron_norms_brute_force_and_repeated_tokens():
+    s, L, P, x = _tiny(B=2, d=8, N=5)
+    y = O.layernorm(x)
+    W1, b1 = np.asarray(L.W1, np.float64), np.asarray(L.b1, np.float64)
+    expect = []
+    for j in range(s.N):
+        acts = [max(0.0, sum(W1[j, c] * y[b, c] for c in range(s.d)) + b1[j]) for b in range(2)]
+        expect.append(math.sqrt(sum(v * v for v in acts)))
+    assert _rel(O.neuron_norms(y, L.W1, L.b1), expect) < 1e-14
+    # the same token twice: sqrt(2) times its single-token norm
+    yy = np.concatenate([y[:1], y[:1]])
+    assert _rel(O.neuron_norms(yy, L.W1, L.b1), math.sqrt(2) * O.neuron_norms(y[:1], L.W1, L.b1)) < 1e-15
+
+
+def test_neuron_with_zero_norm_does_not_change_the_mlp():
+    s, L, P, x = _tiny(B=2)
+    y = O.layernorm(x)
+    nrm = O.neuron_norms(y, L.W1, L.b1)
+    live = np.flatnonzero(nrm > 0)
+    assert len(live) < s.N  # some neurons are off for both tokens at this seed
+    assert _rel(O.sparse_mlp(y, L.W1, L.b1, L.W2, live), O.dense_mlp(y, L.W1, L.b1, L.W2)) < 1e-14
+
+
+def test_head_norms_are_the_slices_of_the_concatenated_heads():
+    # d = h * dh and W^O = I: dense_mha returns the concatenated head outputs itself
+    s, L, P, x = _tiny(B=2, d=24, h=4, dh=6)
+    y = O.layernorm(x)
+    eye = np.eye(s.h * s.dh, dtype=np.float32)
+    Hcat, _, _ = O.dense_mha(y, L.Wqkv, eye, L.K, L.V, s.n, 0.4)
+    expect = np.sqrt((Hcat.reshape(2, s.h, s.dh) ** 2).sum(axis=(0, 2)))
+    assert _rel(O.head_norms(y, L.Wqkv, L.K, L.V, s.n, 0.4), expect) < 1e-14
+
+
+def test_head_norms_empty_cache_is_the_value_norm():
+    s, L, P, x = _tiny(B=1, dtype="f16")
+    y = O.layernorm(x)
+    v = (np.asarray(L.Wqkv[:, 2], np.float64) @ y[0]).astype(np.float16).astype(np.float64)  # [h, dh]
+    assert _rel(O.head_norms(y, L.Wqkv, L.K, L.V, 0, 0.5), np.sqrt((v * v).sum(axis=1))) < 1e-15
+
+
+def test_recall():
+    assert O.recall([1, 2, 3], [2, 3, 4, 5]) == 0.5
+    assert O.recall([], [7]) == 0.0
+    assert O.recall([0, 1], []) == 1.0
+    assert O.recall(np.array([4, 9]), np.array([9, 4])) == 1.0

@@ -83,6 +83,9 @@ def parse(argv=None):
     ap.add_argument("--threshold", action="store_true",
                     help="threshold-mode selection: t calibrated on layer 0's scores to the keep "
                          "percentages; one JSON line with the kept-count spread")
+    ap.add_argument("--recall", action="store_true",
+                    help="the true selection by output norm on every layer of one step: probe time "
+                         "and recall of the predicted sets; one JSON line")
     ap.add_argument("--tp", type=int, default=1,
                     help="time one tensor-parallel shard of the workload split over this many GPUs "
                          "(full predictors, the shard's heads and neurons); one JSON line")
@@ -314,6 +317,71 @@ def sweep(args) -> int:
     return 0
 
 
+def recall_probe(args, wl, s, L, layers, m, desc, ws, x0, lookahead, s_main, k_A, k_M) -> int:
+    """One traced step, then per layer the true sets from output norms (neuron activations
+    on LN(x'), head outputs on LN(x)) and the recall of the predicted sets."""
+    import torch
+    from contextual_sparsity_amd import dejavu as dj
+    import numpy as np
+    dev = "cuda"
+    f = lambda *shape: torch.zeros(*shape, dtype=torch.float32, device=dev)
+    i = lambda *shape: torch.full(shape, -1, dtype=torch.int32, device=dev)
+    t = dict(x_in=f(L, s.B, s.d), x_mid=f(L, s.B, s.d), sets_A=i(L, s.h), sets_M=i(L, s.N), counts=i(L, 2))
+    x = x0.clone()
+    dj.dejavu_stack_decode(m, desc, x, lookahead, False, dj.make_trace(**t), ws, s_main)
+    torch.cuda.synchronize()
+    wt = dj.DJV_F16 if s.dtype == "f16" else dj.DJV_F32
+    pws = dj.workspace(dj.dejavu_workspace_bytes(s.B, s.d, s.N, s.h, s.dh, s.r, s.cap), dev)
+    sws = dj.workspace(4 * ((s.N + 31) // 32) + 256, dev)
+    y = torch.empty(s.B, s.d, device=dev)
+    sc_M, sc_A = torch.empty(s.N, device=dev), torch.empty(s.h, device=dev)
+    idx, cnt = torch.empty(s.N, dtype=torch.int32, device=dev), torch.empty(1, dtype=torch.int32, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    rec_A, rec_M, us_M, us_A = [], [], [], []
+
+    def true_set(scores, n, k):
+        dj.dejavu_select(1, n, scores.view(1, n), dj.DJV_TOPK, k, 0.5, idx, cnt, sws)
+        torch.cuda.synchronize()
+        return set(idx[: int(cnt.item())].cpu().tolist())
+
+    counts = t["counts"].cpu()
+    for l in range(L):
+        w = layers[l]
+        dj.dejavu_layernorm(s.B, s.d, t["x_mid"][l], y, 1e-5)
+        ev[0].record()
+        dj.dejavu_neuron_norms(wt, s.B, s.d, s.N, y, w["W1"], w["b1"], sc_M, pws)
+        ev[1].record()
+        torch.cuda.synchronize()
+        us_M.append(ev[0].elapsed_time(ev[1]) * 1e3)
+        tM = true_set(sc_M, s.N, k_M)
+        dj.dejavu_layernorm(s.B, s.d, t["x_in"][l], y, 1e-5)
+        ev[0].record()
+        dj.dejavu_head_norms(wt, s.B, s.d, s.h, s.dh, s.n, s.cap, y, w["Wqkv"], w["K"], w["V"], wl.scale,
+                             sc_A, pws)
+        ev[1].record()
+        torch.cuda.synchronize()
+        us_A.append(ev[0].elapsed_time(ev[1]) * 1e3)
+        tA = true_set(sc_A, s.h, k_A)
+        pA = set(t["sets_A"][l, : int(counts[l, 0])].cpu().tolist())
+        pM = set(t["sets_M"][l, : int(counts[l, 1])].cpu().tolist())
+        rec_A.append(len(pA & tA) / max(1, len(tA)))
+        rec_M.append(len(pM & tM) / max(1, len(tM)))
+    e = 2 if s.dtype == "f16" else 4
+    bytes_M = s.N * s.d * e
+    bytes_A = 3 * s.h * s.dh * s.d * e + s.B * 2 * s.h * (s.n + 1) * s.dh * e
+    mean = lambda v: float(np.mean(v))
+    out = {"mode": "true-selection recall", "workload": wl.name, "layers": L, "k_A": k_A, "k_M": k_M,
+           "recall_heads": round(mean(rec_A), 4), "recall_neurons": round(mean(rec_M), 4),
+           "chance_heads": round(k_A / s.h, 4), "chance_neurons": round(k_M / s.N, 4),
+           "neuron_norms_us": round(mean(us_M[1:] or us_M), 2),
+           "neuron_norms_GBps": round(bytes_M / (mean(us_M[1:] or us_M) * 1e-6) / 1e9, 1),
+           "head_norms_us": round(mean(us_A[1:] or us_A), 2),
+           "head_norms_GBps": round(bytes_A / (mean(us_A[1:] or us_A) * 1e-6) / 1e9, 1),
+           "note": "untrained synthetic weights: recall near chance is the expected outcome"}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     args = parse(argv)
     if args.gpus != 1:
@@ -437,6 +505,9 @@ def main(argv=None) -> int:
         dj.dejavu_profile_kernel("off")
         d = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(used)]
         return sum(d) / max(1, len(d)), used
+
+    if args.recall:
+        return recall_probe(args, wl, s, L, layers, m, desc, ws, x0, lookahead, s_main, k_A, k_M)
 
     if thr is not None or shard is not None:
         # kept counts vary by layer: bytes from each layer's own counts

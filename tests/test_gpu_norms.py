@@ -37,7 +37,8 @@ def _true_set(scores, k, n):
 
 
 # batches above the vector-ALU limit run on the matrix cores, which need fp16 weights
-CASES = [(n, B) for n in SHAPES for B in (1, 3, 5) if B <= dj.DJV_MAX_VALU_BATCH or SHAPES[n].dtype == "f16"]
+CASES = [(n, B) for n in SHAPES for B in (1, 3, 5)
+         if B <= dj.DJV_MAX_VALU_BATCH or SHAPES[n].dtype == "f16"]
 
 
 @pytest.mark.parametrize("name,B", CASES)

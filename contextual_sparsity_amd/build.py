@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libdejavu.so")
 
 SOURCES = ["api.cpp", "gemv.hip", "gemv_f16.hip", "gemv_f16_side.hip", "gemv_f32.hip",
            "gemv_f32_side.hip", "gemv_dyn_f16.hip", "gemv_dyn_f32.hip", "gemv_mfma.hip", "gather.hip",
-           "axpy.hip", "attn.hip", "select.hip", "norms.hip", "misc.hip"]
+           "axpy.hip", "attn.hip", "select.hip", "norms.hip", "lazykv.hip", "misc.hip"]
 ARCH = "gfx950"
 
 

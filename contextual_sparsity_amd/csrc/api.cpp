@@ -499,6 +499,27 @@ djv_status check_layer(const djv_layer* L, bool dense) {
         DJV_TRY(check_ptr(L->P1_M, "P1_M"));
         DJV_TRY(check_ptr(L->P2_M, "P2_M"));
     }
+    DJV_REQUIRE((L->Y == nullptr) == (L->kv_len == nullptr), DJV_EINVAL,
+                "lazy K/V needs both Y and kv_len (or neither)");
+    if (L->Y) {
+        DJV_TRY(check_ptr(L->Y, "Y"));
+        DJV_TRY(check_idx_ptr(L->kv_len, "kv_len"));
+    }
+    return DJV_OK;
+}
+
+// Lazy K/V of a layer with the step's head list (nothing when the layer has no Y).
+djv_status run_lazy_kv(bool f16, const djv_model& m, const djv_layer& L, const RowInput& in,
+                       const UnitList& heads, hipStream_t s) {
+    if (!L.Y) return DJV_OK;
+    LazyKvArgs a{};
+    a.in = in; a.Y = L.Y;
+    a.kv_prev = L.kv_len + (size_t)(m.n & 1) * m.h;
+    a.kv_next = L.kv_len + (size_t)((m.n + 1) & 1) * m.h;
+    a.heads = heads; a.Wqkv = L.Wqkv; a.Kc = L.Kc; a.Vc = L.Vc;
+    a.B = m.B; a.d = m.d; a.h = m.h; a.dh = m.dh; a.n = m.n; a.n_cap = m.n_cap;
+    a.flags = device_flags();
+    DJV_HIP(launch_lazy_kv(f16, a, s));
     return DJV_OK;
 }
 
@@ -581,6 +602,8 @@ const int32_t* count_of(const djv_model& m, const int32_t* count) {
 djv_status layer_body(const djv_model& m, const djv_layer& L, const LayerIO& io, const LayerWs& w,
                       int buf, bool serial, const djv_trace* tr, int l, hipStream_t s) {
     const bool f16 = m.wt == DJV_F16;
+    DJV_TRY(run_lazy_kv(f16, m, L, ln_input(io.x_in, io.s_in, w, m.eps),
+                        UnitList{w.idxA[buf], count_of(m, w.cntA[buf]), capA_of(m), m.h}, s));
     DJV_TRY(run_mha(f16, m.B, m.d, m.h, m.dh, m.n, m.n_cap, ln_input(io.x_in, io.s_in, w, m.eps),
                     L.Wqkv, L.Wo, L.Kc, L.Vc, w.idxA[buf], count_of(m, w.cntA[buf]),
                     capA_of(m), m.scale, io.x_in, w.xm, w.sm, w.mha, s));
@@ -938,6 +961,8 @@ djv_status dejavu_stack_decode(const djv_model* m, const djv_layer* layers, int 
             const djv_layer& Ly = layers[l];
             const LayerIO io = layer_io(x, w, l, L);
             DJV_TRY(trace_x(trace, *m, l, io.x_in, sm));
+            DJV_TRY(run_lazy_kv(f16, *m, Ly, ln_input(io.x_in, io.s_in, w, m->eps),
+                                UnitList{nullptr, nullptr, m->h, m->h}, sm));
             DJV_TRY(run_mha(f16, m->B, m->d, m->h, m->dh, m->n, m->n_cap,
                             ln_input(io.x_in, io.s_in, w, m->eps), Ly.Wqkv, Ly.Wo, Ly.Kc, Ly.Vc,
                             nullptr, nullptr, m->h, m->scale, io.x_in, w.xm, w.sm, w.mha, sm));
@@ -992,6 +1017,7 @@ djv_status dejavu_stack_decode(const djv_model* m, const djv_layer* layers, int 
             nm = job_M(*m, layers[l + 1], w, nxt, trace, l + 1);
         }
         DJV_TRY(trace_x(trace, *m, l, io.x_in, sm));
+        DJV_TRY(run_lazy_kv(f16, *m, Ly, in_a, heads, sm));
 
         // Q/K/V of the kept heads (+ K/V append), P1 of both predictors for l+1, S_M^l
         GemvArgs g = gemv_args(m->d, m->B, DJV_PROF_QKV, w.mf);

@@ -348,6 +348,22 @@ int attn_chunk_for(bool f16, int dh);  // positions per attention chunk
 
 hipError_t launch_select(const SelectJob* jobs, int njobs, int B, hipStream_t s, int prof);
 
+// Lazy K/V of the heads a step does not select (lazykv.hip): saves the step's attention
+// input and recomputes the selected heads' missing K/V from the saved inputs.
+struct LazyKvArgs {
+    RowInput in;             // the layer's attention input (y ready, or x with tile stats)
+    float* Y;                // [B, n_cap, d] saved inputs
+    const int32_t* kv_prev;  // [h] positions with valid K/V before this step
+    int32_t* kv_next;        // [h] after it
+    UnitList heads;          // the selected heads
+    const void* Wqkv;        // [h, 3, dh, d]
+    void* Kc;                // [B, h, n_cap, dh]
+    void* Vc;
+    int B, d, h, dh, n, n_cap;
+    unsigned* flags;
+};
+hipError_t launch_lazy_kv(bool f16, const LazyKvArgs& a, hipStream_t s);
+
 hipError_t launch_layernorm(int B, int d, const float* x, float* y, float eps, hipStream_t s);
 // (mean, M2) of each kLnTile-column slice of x [B, d].
 hipError_t launch_ln_stats(int B, int d, const float* x, float2* stats, hipStream_t s);

@@ -111,7 +111,6 @@ __device__ __forceinline__ void row_moments(const RowInput& in, int cols, int b,
     rstd = 1.0f / sqrtf(wave_sum(qs) / (float)cols + in.eps);
 }
 
-// Writes the result of visited row r (weight unit `unit`, -1 when skipped) for batch row b.
 // What a group's weight loads need of its segment, and what its stores need: small
 // enough to keep every segment's copy in scalar registers and pick one by a uniform select.
 struct SegRows {
@@ -136,6 +135,7 @@ __device__ __forceinline__ Seg pick3(int i, const Seg& s0, const Seg& s1, const 
     return i == 0 ? s0 : (i == 1 ? s1 : s2);
 }
 
+// Writes the result of visited row r (weight unit `unit`, -1 when skipped) for batch row b.
 template <typename T>
 __device__ __forceinline__ void epilogue(const GemvArgs& a, const SegOut& S, int r, int b, float acc,
                                          int unit, float bias) {

@@ -1,0 +1,97 @@
+// Lazy K/V for the heads a step does not select.
+//
+// [NOTES "Sparsity operator for Attention"]: a step computes and stores K/V only for the
+// predicted heads S_A, and keeps a copy of its attention input y for the other heads;
+// when a head that skipped earlier steps is selected again, its missing K/V are computed
+// from the saved inputs before it attends.  The cache then holds, for every head, what
+// computing all heads' K/V at every step would have stored.
+//
+// One launch per layer and step at position n, before the layer's Q/K/V launch:
+//   blocks [0, B):      Y[b, n] = y[b] (the normalised input, as the Q/K/V GEMV forms it);
+//   block B:            kv_next[i] = n + 1 for the selected heads, kv_prev[i] otherwise;
+//   the other blocks:   for each selected head i and each position p in [kv_prev[i], n),
+//                       K[b, i, p] = W_i^K Y[b, p] and V[b, i, p] = W_i^V Y[b, p], rounded
+//                       to the cache type; a wave per output row (K or V column c).
+// kv_len holds two buffers of h entries read and written alternately by the parity of n,
+// so no block reads an entry that another block of the same launch writes.
+#include "gemv.hpp"
+
+namespace djv {
+
+namespace {
+
+constexpr int kLazyThreads = 256;
+constexpr int kLazyRows = kLazyThreads / kWave;  // output rows per block (a wave each)
+
+template <typename T>
+__global__ __launch_bounds__(kLazyThreads) void lazy_kv_kernel(LazyKvArgs a) {
+    const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+    const int bid = blockIdx.x;
+    if (bid < a.B) {
+        // save this step's input row b, normalised as the Q/K/V launch normalises it
+        const int b = bid;
+        float* dst = a.Y + ((size_t)b * a.n_cap + a.n) * a.d;
+        if (a.in.y) {
+            for (int e = tid; e < a.d; e += kLazyThreads) dst[e] = a.in.y[(size_t)b * a.d + e];
+        } else {
+            float mean, rstd;
+            gemv_detail::row_moments(a.in, a.d, b, mean, rstd);
+            const float* x = a.in.x + (size_t)b * a.d;
+            for (int e = tid; e < a.d; e += kLazyThreads) dst[e] = (x[e] - mean) * rstd;
+        }
+        return;
+    }
+    const int count = read_count(a.heads, a.flags);
+    if (bid == a.B) {
+        for (int i = tid; i < a.h; i += kLazyThreads) a.kv_next[i] = a.kv_prev[i];
+        __syncthreads();
+        for (int u = tid; u < count; u += kLazyThreads) {
+            const int i = unit_of(a.heads, u, a.flags);
+            if (i >= 0) a.kv_next[i] = a.n + 1;
+        }
+        return;
+    }
+    // catch-up: output row j of head slot u (j < dh: K column j, else V column j - dh)
+    const int rows_per_head = 2 * a.dh;
+    const int g = (bid - a.B - 1) * kLazyRows + wv;
+    const int u = g / rows_per_head, j = g - u * rows_per_head;
+    if (u >= count) return;  // uniform over the wave
+    const int i = unit_of(a.heads, u, a.flags);
+    if (i < 0) return;
+    const int part = 1 + j / a.dh, c = j % a.dh;
+    const int start = max(a.kv_prev[i], 0);
+    if (start >= a.n) return;
+    constexpr int E = WTraits<T>::kPerVec;
+    const T* W = reinterpret_cast<const T*>(a.Wqkv) + (((size_t)i * 3 + part) * a.dh + c) * a.d;
+    T* cache = reinterpret_cast<T*>(part == 1 ? a.Kc : a.Vc);
+    for (int p = start; p < a.n; ++p) {
+        for (int b = 0; b < a.B; ++b) {
+            const float* y = a.Y + ((size_t)b * a.n_cap + p) * a.d;
+            float acc = 0.f;
+            for (int e0 = lane * E; e0 < a.d; e0 += kWave * E) {
+                float w[E];
+                unpack<T>(*reinterpret_cast<const Vec16*>(W + e0), w);
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc = fmaf(w[e], y[e0 + e], acc);
+            }
+            acc = wave_sum(acc);
+            if (lane == 0) cache[(((size_t)b * a.h + i) * a.n_cap + p) * a.dh + c] = to_store<T>(acc);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_lazy_kv(bool f16, const LazyKvArgs& a, hipStream_t s) {
+    if (a.B < 1 || a.d < 1 || a.h < 1 || a.n < 0 || a.n >= a.n_cap || a.heads.cap < 1)
+        return hipErrorInvalidValue;
+    const long long rows = (long long)a.heads.cap * 2 * a.dh;
+    const dim3 grid((unsigned)(a.B + 1 + (rows + kLazyRows - 1) / kLazyRows));
+    if (f16)
+        hipLaunchKernelGGL(lazy_kv_kernel<__half>, grid, dim3(kLazyThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL(lazy_kv_kernel<float>, grid, dim3(kLazyThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace djv

@@ -57,7 +57,8 @@ class djv_model(ctypes.Structure):
 
 class djv_layer(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in
-                ("Wqkv", "Wo", "W1", "b1", "W2", "Kc", "Vc", "P1_A", "P2_A", "P1_M", "P2_M")]
+                ("Wqkv", "Wo", "W1", "b1", "W2", "Kc", "Vc", "P1_A", "P2_A", "P1_M", "P2_M",
+                 "Y", "kv_len")]
 
 
 class djv_trace(ctypes.Structure):
@@ -261,7 +262,7 @@ def make_layer(w: dict, p: Optional[dict] = None) -> djv_layer:
     get = lambda dct, k: _ptr(dct.get(k))
     return djv_layer(get(w, "Wqkv"), get(w, "Wo"), get(w, "W1"), get(w, "b1"), get(w, "W2"),
                      get(w, "K"), get(w, "V"), get(p, "P1_A"), get(p, "P2_A"), get(p, "P1_M"),
-                     get(p, "P2_M"))
+                     get(p, "P2_M"), get(w, "Y"), get(w, "kv_len"))
 
 
 def make_trace(x_in=None, x_mid=None, z_A=None, z_M=None, sets_A=None, sets_M=None,

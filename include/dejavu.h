@@ -224,6 +224,15 @@ typedef struct djv_layer {
     void* Kc; void* Vc;                         /* this layer's KV cache */
     const void* P1_A; const void* P2_A;         /* head predictor [r,d], [h,r] */
     const void* P1_M; const void* P2_M;         /* neuron predictor [r,d], [N,r] */
+    /* Lazy K/V (both NULL: off).  [NOTES "Sparsity operator for Attention"]: a step
+     * stores K/V only for its selected heads and keeps its attention input y for the
+     * others; a head selected again first gets its missing K/V computed from the kept
+     * inputs.  Y [B, n_cap, d] fp32: the layer's y of every position (written at n by each
+     * step).  kv_len [2, h] int32: per head, the number of positions whose K/V are valid;
+     * a step at position n reads half (n & 1) and writes half ((n + 1) & 1), so set both
+     * halves to the filled length (n of the first step) before it.  With lazy K/V every
+     * selected head attends over the K/V that computing all heads at every step gives. */
+    float* Y; int32_t* kv_len;
 } djv_layer;
 
 typedef struct djv_model {

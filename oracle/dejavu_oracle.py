@@ -280,6 +280,26 @@ def dense_mha(y, Wqkv, Wo, K, V, n: int, scale: float):
     return Hcat @ _f64(Wo), Kn, Vn
 
 
+def cache_after_steps(Wqkv, K0, V0, n0: int, ys) -> Tuple[np.ndarray, np.ndarray]:
+    """The K/V cache after decode steps at positions n0, n0+1, ... with attention inputs
+    ys[t] [B, d]: positions below n0 as in K0 / V0, position n0 + t holding every head's
+    round(W_i^K ys[t]) and round(W_i^V ys[t]) in the cache dtype.
+
+    [NOTES "Sparsity operator for Attention"]: a step stores K/V only for its selected
+    heads and keeps y for the others, recomputing their K/V from it when they are
+    selected later; a head attending at a later step therefore sees exactly these
+    entries.  This is the plain definition that lazy recomputation must reach.
+    """
+    K, V = np.array(K0, copy=True), np.array(V0, copy=True)
+    for t, y in enumerate(ys):
+        y = _f64(y)
+        k = np.einsum("icd,bd->bic", _f64(Wqkv[:, 1]), y)
+        v = np.einsum("icd,bd->bic", _f64(Wqkv[:, 2]), y)
+        K[:, :, n0 + t] = _round_to(k, K.dtype)
+        V[:, :, n0 + t] = _round_to(v, V.dtype)
+    return K, V
+
+
 # --------------------------------------------------------------------------------------
 # "True" selection by output norm  [BLOG §1 "Contextual Sparsity"]
 # --------------------------------------------------------------------------------------

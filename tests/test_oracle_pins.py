@@ -480,3 +480,28 @@ def test_recall():
     assert O.recall([], [7]) == 0.0
     assert O.recall([0, 1], []) == 1.0
     assert O.recall(np.array([4, 9]), np.array([9, 4])) == 1.0
+
+
+# ------------------------------------------------------------------------------ lazy K/V
+def test_cache_after_steps_holds_each_steps_dense_kv():
+    s, L, P, x = _tiny(B=2, dtype="f16", n=3, n_cap=8)
+    ys = [O.layernorm(synth.make_input(s, 10 + t).numpy()) for t in range(4)]
+    K, V = O.cache_after_steps(L.Wqkv, L.K, L.V, 3, ys)
+    assert K.dtype == L.K.dtype
+    assert np.array_equal(K[:, :, :3], L.K[:, :, :3]) and np.array_equal(K[:, :, 7:], L.K[:, :, 7:])
+    for t, y in enumerate(ys):
+        # dense attention computes (and rounds) every head's K/V of its input
+        _, kn, vn = O.dense_mha(y, L.Wqkv, L.Wo, L.K, L.V, 3, 0.5)
+        assert np.array_equal(K[:, :, 3 + t], kn) and np.array_equal(V[:, :, 3 + t], vn)
+
+
+def test_attention_over_the_steps_cache_is_sparse_mha_at_the_last_step():
+    # the last step's sparse attention appends its own K/V: over the cache of the earlier
+    # steps it equals attending the full cache of all steps up to and including it
+    s, L, P, x = _tiny(B=1, n=3, n_cap=8)
+    ys = [O.layernorm(synth.make_input(s, 20 + t).numpy()) for t in range(3)]
+    K, V = O.cache_after_steps(L.Wqkv, L.K, L.V, 3, ys)
+    out, _, _ = O.sparse_mha(ys[2], L.Wqkv, L.Wo, K, V, 5, [1, 3], 0.7)
+    K2, V2 = O.cache_after_steps(L.Wqkv, L.K, L.V, 3, ys[:2])
+    out2, _, _ = O.sparse_mha(ys[2], L.Wqkv, L.Wo, K2, V2, 5, [1, 3], 0.7)
+    assert _rel(out, out2) < 1e-15

@@ -385,7 +385,7 @@ def recall_probe(args, wl, s, L, layers, m, desc, ws, x0, lookahead, s_main, k_A
 def main(argv=None) -> int:
     args = parse(argv)
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no "
               "multi-GPU path", file=sys.stderr)
         return 2
     if args.sweep:

@@ -74,7 +74,7 @@ djv_status check_dtype(int wt) {
 }
 djv_status check_batch(int B) {
     DJV_REQUIRE(B >= 1, DJV_EINVAL, "B must be >= 1 (got %d)", B);
-    DJV_REQUIRE(B <= DJV_MAX_BATCH, DJV_EUNSUPPORTED, "B = %d exceeds this build's limit %d", B, DJV_MAX_BATCH);
+    DJV_REQUIRE(B <= DJV_MAX_BATCH, DJV_EUNSUPPORTED, "B = %d exceeds the library's limit %d", B, DJV_MAX_BATCH);
     return DJV_OK;
 }
 // Batches above kMaxBatch run on the matrix cores: fp16 weights, and every GEMV row length

@@ -53,7 +53,7 @@ typedef enum {
     DJV_EINVAL = -1,       /* bad dimension, pointer, mode, k or t */
     DJV_EALIGN = -2,       /* a tensor pointer is not 16-byte aligned (ws: 256) */
     DJV_EWORKSPACE = -3,   /* ws_bytes below dejavu_workspace_bytes() */
-    DJV_EUNSUPPORTED = -4, /* valid but outside this build's limits (see each call) */
+    DJV_EUNSUPPORTED = -4, /* valid but outside the library's limits (see each call) */
     DJV_EHIP = -5          /* a HIP runtime call or kernel launch failed */
 } djv_status;
 
@@ -68,7 +68,7 @@ typedef enum {
 #define DJV_FLAG_BAD_INDEX 1u  /* an index list held a value outside [0, units) */
 #define DJV_FLAG_BAD_COUNT 2u  /* a device count exceeded its list's capacity */
 
-/* Limits of this build (DJV_EUNSUPPORTED beyond them):
+/* Limits of the library (DJV_EUNSUPPORTED beyond them):
  *   B <= DJV_MAX_BATCH; d and r multiples of 8 with d*esize <= 32768 bytes and
  *   r*esize <= 32768 bytes (one row fits 256 threads x 8 x 16-byte loads); dh in {64, 128};
  *   n_out <= 65536 for selection.

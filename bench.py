@@ -594,8 +594,18 @@ def main(argv=None) -> int:
     eb.record()
     torch.cuda.synchronize()
     copy_gbs = 2 * src.numel() * 4 * 5 / (ea.elapsed_time(eb) * 1e-3) / 1e9
+    # plain read rate: the library's streaming-read kernel over the same 2 GiB
+    probe_out = torch.zeros(1, dtype=torch.int32, device=dev)
+    dj.dejavu_read_probe(src, probe_out, stream=s_main)
+    torch.cuda.synchronize()
+    ea.record(s_main)
+    for _ in range(5):
+        dj.dejavu_read_probe(src, probe_out, stream=s_main)
+    eb.record(s_main)
+    torch.cuda.synchronize()
+    read_gbs = src.numel() * 4 * 5 / (ea.elapsed_time(eb) * 1e-3) / 1e9
     del src, dst
-    log(f"device copy reference {copy_gbs:.0f} GB/s (read + write)")
+    log(f"device copy reference {copy_gbs:.0f} GB/s (read + write), plain read {read_gbs:.0f} GB/s")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -623,6 +633,8 @@ def main(argv=None) -> int:
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "copy_ref_GBps": round(copy_gbs, 1),
         "pct_of_copy_ref": round(100 * gbs / copy_gbs, 2),
+        "read_ref_GBps": round(read_gbs, 1),
+        "pct_of_read_ref": round(100 * gbs / read_gbs, 2),
         "tokens_per_s": round(1e3 / ms_step, 1),
         "bytes_per_layer": lb,
         "wall_ms_per_step": round(wall_ms, 4),

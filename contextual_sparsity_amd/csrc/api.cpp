@@ -26,6 +26,8 @@ hipError_t launch_gather_rows(const void* W, void* out, const UnitList& list, in
                               unsigned* flags, hipStream_t s);
 // norms.hip: scores[u] = sqrt(sum over b and c of v[b, u, c]^2), v [B, units, w] fp32.
 hipError_t launch_unit_norms(const float* v, int B, int units, int w, float* scores, hipStream_t s);
+// misc.hip: plain streaming read of `bytes` (a multiple of 16) from buf.
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* out, hipStream_t s);
 }  // namespace djv
 
 namespace {
@@ -1084,6 +1086,14 @@ djv_status dejavu_profile_kernel(int family, void* const* events, int capacity) 
     h.cap = capacity;
     h.used = 0;
     h.open = false;
+    return DJV_OK;
+}
+
+djv_status dejavu_read_probe(const void* buf, size_t bytes, uint32_t* out, void* stream) {
+    DJV_REQUIRE(buf != nullptr && out != nullptr, DJV_EINVAL, "buf and out must not be NULL");
+    DJV_REQUIRE(bytes > 0 && bytes % 16 == 0, DJV_EINVAL, "bytes = %zu must be a positive multiple of 16", bytes);
+    DJV_REQUIRE(aligned(buf, 16) && aligned(out, 4), DJV_EALIGN, "buf must be 16-byte and out 4-byte aligned");
+    DJV_HIP(launch_read_probe(buf, bytes, out, (hipStream_t)stream));
     return DJV_OK;
 }
 

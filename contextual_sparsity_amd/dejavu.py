@@ -32,7 +32,7 @@ EXPORTS = [
     "dejavu_sparse_mha", "dejavu_dense_mha", "dejavu_neuron_norms", "dejavu_head_norms",
     "dejavu_sparse_layer", "dejavu_stack_decode", "dejavu_poll_device_error",
     "dejavu_set_mfma_min_batch", "dejavu_gather_rows", "dejavu_profile_kernel", "dejavu_profile_count",
-    "dejavu_last_error", "dejavu_version",
+    "dejavu_read_probe", "dejavu_last_error", "dejavu_version",
 ]
 
 DJV_PROF = {"off": 0, "qkv": 1, "mlp_up": 2, "mlp_down": 3, "o_proj": 4, "attn": 5, "pred_1": 6,
@@ -102,6 +102,7 @@ def lib() -> ctypes.CDLL:
             "dejavu_gather_rows": [_I, _I, _I, _I, _P, _P, _P, _I, _P, _P],
             "dejavu_profile_kernel": [_I, ctypes.POINTER(_P), _I],
             "dejavu_profile_count": [ctypes.POINTER(_I)],
+            "dejavu_read_probe": [_P, _SZ, _P, _P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -335,3 +336,11 @@ def dejavu_profile_count() -> int:
 
 
 _PROF_KEEP = None
+
+
+def dejavu_read_probe(buf, out, nbytes=None, stream=None) -> None:
+    """Plain streaming read of ``nbytes`` of ``buf`` (default: the whole device tensor; a
+    multiple of 16 bytes); ``out`` is a one-element 32-bit device tensor (see the header)."""
+    if nbytes is None:
+        nbytes = buf.numel() * buf.element_size()
+    _check(lib().dejavu_read_probe(_ptr(buf), ctypes.c_size_t(nbytes), _ptr(out), _stream(stream)))

@@ -341,6 +341,19 @@ djv_status dejavu_set_mfma_min_batch(int b, int* previous);
 djv_status dejavu_profile_kernel(int family, void* const* events, int capacity);
 djv_status dejavu_profile_count(int* count);
 
+/* --------------------------------------------------------------------------------------
+ * dejavu_read_probe -- benchmark reference: reads `bytes` of buf once with 16-byte
+ *   non-temporal loads (the load form of the weight streams above), every block of a
+ *   grid of 8 blocks per compute unit streaming one contiguous share, and folds the data
+ *   into one word.  out (device, one
+ *   uint32) is written only when that word equals an arbitrary fixed value, which keeps
+ *   the loads from being removed; its contents are not a result.  The rate of this call
+ *   is the plain HBM read rate that the sparse layer's rate on its touched bytes is
+ *   compared with.  buf: device, 16-byte aligned, bytes a positive multiple of 16 (else
+ *   DJV_EINVAL / DJV_EALIGN).  Enqueues one kernel on `stream`.
+ * ------------------------------------------------------------------------------------ */
+djv_status dejavu_read_probe(const void* buf, size_t bytes, uint32_t* out, void* stream);
+
 /* dejavu_last_error -- message of this thread's last failing call ("" if none). */
 const char* dejavu_last_error(void);
 

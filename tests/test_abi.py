@@ -212,3 +212,13 @@ def test_gather_rows_argument_errors():
     assert call(count=A + 2) == dj.DJV_EALIGN
     assert call(out=MIS) == dj.DJV_EALIGN          # 1536-byte rows need 16-byte alignment
     assert call(cols=2, out=A + 2) == dj.DJV_EALIGN  # 4-byte rows need 4-byte alignment
+
+
+def test_read_probe_argument_errors():
+    p = dj.dejavu_read_probe
+    assert _status(p, A, A, nbytes=0) == dj.DJV_EINVAL
+    assert _status(p, A, A, nbytes=24) == dj.DJV_EINVAL      # not a multiple of 16
+    assert _status(p, None, A, nbytes=64) == dj.DJV_EINVAL
+    assert _status(p, A, None, nbytes=64) == dj.DJV_EINVAL
+    assert _status(p, A + 8, A, nbytes=64) == dj.DJV_EALIGN
+    assert _status(p, A, A + 2, nbytes=64) == dj.DJV_EALIGN

@@ -80,6 +80,8 @@ def parse(argv=None):
     ap.add_argument("--sweep-layers", type=int, default=8, help="distinct layers per sweep step")
     ap.add_argument("--sweep-steps", type=int, default=5)
     ap.add_argument("--sweep-batches", default="", help="comma list overriding the sweep's batches")
+    ap.add_argument("--sweep-pct-a", default="", help="comma list overriding the head keep-percentages")
+    ap.add_argument("--sweep-pct-m", default="", help="comma list overriding the neuron keep-percentages")
     ap.add_argument("--threshold", action="store_true",
                     help="threshold-mode selection: t calibrated on layer 0's scores to the keep "
                          "percentages; one JSON line with the kept-count spread")
@@ -233,6 +235,16 @@ def union_bytes(s, B, uA, uM):
     return pred + 4 * s.d * s.dh * uA * e + B * 2 * (s.n + 1) * s.dh * uA * e + 2 * uM * s.d * e + uM * e
 
 
+def union_weight_elems(s, uA, uM):
+    """Weight elements of the products (predictors, Q/K/V, O, MLP) at union sizes uA, uM:
+    each carries one multiply-add per batch row, on the matrix cores in their form."""
+    pred = 2 * s.d * s.r + s.r * s.N + s.r * s.h
+    return pred + 4 * s.d * s.dh * uA + 2 * uM * s.d
+
+
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak, AMD published
+
+
 def sweep(args) -> int:
     import torch
     from contextual_sparsity_amd import configs, synth
@@ -287,8 +299,10 @@ def sweep(args) -> int:
         for form in forms:
             dj.dejavu_set_mfma_min_batch(1 if form == "mfma" else dj.DJV_MAX_VALU_BATCH + 1)
             dense_us[form] = run(m_dense, x, x0, True, max(2, args.sweep_steps // 2))
-        for pA in configs.SWEEP_PCT_A:
-            for pM in configs.SWEEP_PCT_M:
+        pcts_A = [int(p) for p in args.sweep_pct_a.split(",")] if args.sweep_pct_a else list(configs.SWEEP_PCT_A)
+        pcts_M = [int(p) for p in args.sweep_pct_m.split(",")] if args.sweep_pct_m else list(configs.SWEEP_PCT_M)
+        for pA in pcts_A:
+            for pM in pcts_M:
                 kA, kM = configs.keep(pA, s.h), configs.keep(pM, s.N)
                 m = dj.make_model(dj.DJV_F16, B, s.d, s.N, s.h, s.dh, s.r, s.n, s.cap, base.scale,
                                   dj.DJV_TOPK, kA, kM)
@@ -306,6 +320,11 @@ def sweep(args) -> int:
                     us = run(m, x, x0, False, args.sweep_steps)
                     pt[f"{form}_us"] = round(us, 2)
                     pt[f"{form}_GBps"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+                    if form == "mfma":
+                        # algorithmic matrix rate of the layer: 2*B flops per weight element
+                        tf = 2 * B * union_weight_elems(s, uA, uM) / (us * 1e-6) / 1e12
+                        pt["mfma_TFLOPs_alg"] = round(tf, 2)
+                        pt["mfma_pct_of_peak_alg"] = round(100 * tf / MFMA_F16_PEAK_TFLOPS, 3)
                     pt[f"{form}_dense_us"] = round(dense_us[form], 2)
                 best = min(forms, key=lambda f: pt[f"{f}_us"])
                 pt["best"] = best

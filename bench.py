@@ -153,12 +153,29 @@ def cpu_baseline(wl, s, layers_gpu, preds_gpu, x0, k_A, k_M, budget_s, lb):
         if t_total >= budget_s:
             break
     per_layer_s = t_total / done
+    # the first layer again on one thread (numpy's BLAS pool limited to 1)
+    one_thread_s = None
+    try:
+        from threadpoolctl import threadpool_limits
+        x1 = host(x0).astype(np.float64)
+        Lw = O.LayerWeights(**{k: host(v) for k, v in layers_gpu[0].items()})
+        Pw = O.PredictorWeights(**{k: host(v) for k, v in preds_gpu[0].items()})
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            y1 = O.layernorm(x1)
+            S_A, S_M = O.predict_sets(y1, Pw, sel)
+            O.sparse_layer(x1, Lw, S_A, S_M, s.n, wl.scale)
+            one_thread_s = time.perf_counter() - t0
+        del Lw, Pw
+    except ImportError:  # pragma: no cover
+        pass
     return {
         "value": round(lb / per_layer_s / 1e9, 4), "unit": "GB/s",
         "us_per_layer": round(per_layer_s * 1e6, 1),
         "cores": int(threads), "host_cpus": os.cpu_count(), "kind": "oracle",
+        "one_thread_us_per_layer": round(one_thread_s * 1e6, 1) if one_thread_s else None,
         "sample": f"first {done} of {len(layers_gpu)} layers of one decode step (float64 numpy "
-                  f"oracle, lookahead sets), {t_total:.1f} s of CPU work",
+                  f"oracle, lookahead sets), {t_total:.1f} s of CPU work; layer 0 again on one thread",
     }
 
 

@@ -94,6 +94,9 @@ def parse(argv=None):
     ap.add_argument("--tp-rank", type=int, default=0, help="which shard --tp times")
     ap.add_argument("--ablation", action="store_true",
                     help="the fusion ablation: fused sparse MLP vs gather-then-dense, OPT-175B shape")
+    ap.add_argument("--lazy-kv", action="store_true",
+                    help="decode steps with n advancing, with and without lazy K/V of skipped heads")
+    ap.add_argument("--lazy-steps", type=int, default=16, help="decode steps of --lazy-kv")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 1 GiB three times (reference for HBM byte "
                          "counters) and exit")
@@ -353,6 +356,77 @@ def sweep(args) -> int:
     return 0
 
 
+def lazy_kv(args) -> int:
+    """Decode steps at positions n0, n0+1, ... through the stack (a fresh seeded token each
+    step), once without and once with lazy K/V: with it, each step saves its attention
+    inputs and a selected head first recomputes the K/V of the positions it skipped.
+    Reports µs per layer per step for both, and the K/V positions recomputed per step."""
+    import torch
+    from contextual_sparsity_amd import configs, synth
+    from contextual_sparsity_amd import dejavu as dj
+
+    wl = configs.WORKLOADS[args.workload]
+    T = args.lazy_steps
+    L = args.layers or wl.layers
+    s = wl.shape.with_(n_cap=wl.shape.n + T + 1)
+    n0, dev = s.n, "cuda"
+    t0 = time.time()
+    layers, preds = [], []
+    for l in range(L):
+        layers.append(synth.make_layer(s, args.seed, l, dev))
+        preds.append(synth.make_predictors(s, args.seed, l, dev))
+    for w in layers:
+        w["Y"] = torch.zeros(s.B, s.cap, s.d, dtype=torch.float32, device=dev)
+        w["kv_len"] = torch.full((2, s.h), n0, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    log(f"lazy K/V: {L} layers, cache capacity {s.cap} ({time.time() - t0:.1f} s, "
+        f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB)")
+    wt = dj.DJV_F16 if s.dtype == "f16" else dj.DJV_F32
+    plain = [dj.make_layer({k: v for k, v in layers[l].items() if k not in ("Y", "kv_len")}, preds[l])
+             for l in range(L)]
+    lazy = [dj.make_layer(layers[l], preds[l]) for l in range(L)]
+    tokens = [synth.make_input(s, args.seed + 1000 + t, dev) for t in range(T)]
+    models = [dj.make_model(wt, s.B, s.d, s.N, s.h, s.dh, s.r, n0 + t, s.cap, wl.scale, dj.DJV_TOPK,
+                            wl.k_A, wl.k_M) for t in range(T)]
+    ws = dj.workspace(dj.dejavu_workspace_bytes_model(models[-1]), dev)
+    stream = torch.cuda.current_stream()
+    x = tokens[0].clone()
+    out = {"mode": "lazy K/V decode", "workload": wl.name, "layers": L, "steps": T, "n0": n0}
+    for name, desc in (("plain", plain), ("lazy", lazy)):
+        for w in layers:
+            w["kv_len"].fill_(n0)
+        x.copy_(tokens[0])
+        dj.dejavu_stack_decode(models[0], desc, x, True, False, None, ws, stream)  # warm-up
+        for w in layers:
+            w["kv_len"].fill_(n0)
+        us, recomputed = [], []
+        for t in range(T):
+            # a step at position n reads the lengths in half n % 2 and writes half (n + 1) % 2
+            n = n0 + t
+            before = torch.stack([w["kv_len"][n % 2] for w in layers]) if name == "lazy" else None
+            x.copy_(tokens[t])
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            dj.dejavu_stack_decode(models[t], desc, x, True, False, None, ws, stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            us.append(a.elapsed_time(b) * 1e3 / L)
+            if name == "lazy":
+                # heads selected at step t: valid length n0+t+1 after it; each recomputed
+                # the positions between its previous valid length and n0+t
+                after = torch.stack([w["kv_len"][(n + 1) % 2] for w in layers])
+                sel = after == n + 1
+                recomputed.append(int(((n - before).clamp(min=0) * sel).sum().item()))
+        out[f"{name}_us_per_layer"] = round(sum(us) / T, 2)
+        out[f"{name}_us_per_layer_first_last"] = [round(us[0], 2), round(us[-1], 2)]
+        if name == "lazy":
+            out["kv_positions_recomputed_per_step"] = round(sum(recomputed) / T, 1)
+            out["kv_positions_recomputed_by_step"] = recomputed
+    out["lazy_overhead_us_per_layer"] = round(out["lazy_us_per_layer"] - out["plain_us_per_layer"], 2)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def recall_probe(args, wl, s, L, layers, m, desc, ws, x0, lookahead, s_main, k_A, k_M) -> int:
     """One traced step, then per layer the true sets from output norms (neuron activations
     on LN(x'), head outputs on LN(x)) and the recall of the predicted sets."""
@@ -426,6 +500,8 @@ def main(argv=None) -> int:
         return 2
     if args.sweep:
         return sweep(args)
+    if args.lazy_kv:
+        return lazy_kv(args)
     if args.ablation:
         return ablation(args)
     import torch

@@ -22,6 +22,8 @@ namespace {
 
 constexpr int kLazyThreads = 256;
 constexpr int kLazyRows = kLazyThreads / kWave;  // output rows per block (a wave each)
+constexpr int kSaveBatch = 16;  // values of the saved input per thread in flight
+constexpr int kDotBatch = 8;    // 16-byte weight vectors (and their inputs) per lane in flight
 
 template <typename T>
 __global__ __launch_bounds__(kLazyThreads) void lazy_kv_kernel(LazyKvArgs a) {
@@ -29,15 +31,25 @@ __global__ __launch_bounds__(kLazyThreads) void lazy_kv_kernel(LazyKvArgs a) {
     const int bid = blockIdx.x;
     if (bid < a.B) {
         // save this step's input row b, normalised as the Q/K/V launch normalises it
+        // (loads batched ahead of the stores: the source and Y may not be assumed apart,
+        // so a plain copy loop would wait for each load in turn)
         const int b = bid;
         float* dst = a.Y + ((size_t)b * a.n_cap + a.n) * a.d;
-        if (a.in.y) {
-            for (int e = tid; e < a.d; e += kLazyThreads) dst[e] = a.in.y[(size_t)b * a.d + e];
-        } else {
-            float mean, rstd;
-            gemv_detail::row_moments(a.in, a.d, b, mean, rstd);
-            const float* x = a.in.x + (size_t)b * a.d;
-            for (int e = tid; e < a.d; e += kLazyThreads) dst[e] = (x[e] - mean) * rstd;
+        float mean = 0.f, rstd = 1.f;
+        if (!a.in.y) gemv_detail::row_moments(a.in, a.d, b, mean, rstd);
+        const float* src = (a.in.y ? a.in.y : a.in.x) + (size_t)b * a.d;
+        for (int e0 = tid; e0 < a.d; e0 += kLazyThreads * kSaveBatch) {
+            float v[kSaveBatch];
+#pragma unroll
+            for (int k = 0; k < kSaveBatch; ++k) {
+                const int e = e0 + k * kLazyThreads;
+                v[k] = e < a.d ? src[e] : 0.f;
+            }
+#pragma unroll
+            for (int k = 0; k < kSaveBatch; ++k) {
+                const int e = e0 + k * kLazyThreads;
+                if (e < a.d) dst[e] = (v[k] - mean) * rstd;
+            }
         }
         return;
     }
@@ -64,15 +76,39 @@ __global__ __launch_bounds__(kLazyThreads) void lazy_kv_kernel(LazyKvArgs a) {
     constexpr int E = WTraits<T>::kPerVec;
     const T* W = reinterpret_cast<const T*>(a.Wqkv) + (((size_t)i * 3 + part) * a.dh + c) * a.d;
     T* cache = reinterpret_cast<T*>(part == 1 ? a.Kc : a.Vc);
+    const int nvec = a.d / E;  // 16-byte weight vectors per row (d % 8 == 0)
     for (int p = start; p < a.n; ++p) {
         for (int b = 0; b < a.B; ++b) {
             const float* y = a.Y + ((size_t)b * a.n_cap + p) * a.d;
+            // lane's vectors v = lane, lane + 64, ... in order, kDotBatch of them (weights
+            // and inputs) requested before the first multiply
             float acc = 0.f;
-            for (int e0 = lane * E; e0 < a.d; e0 += kWave * E) {
-                float w[E];
-                unpack<T>(*reinterpret_cast<const Vec16*>(W + e0), w);
+            for (int v0 = lane; v0 < nvec; v0 += kWave * kDotBatch) {
+                Vec16 wv[kDotBatch];
+                float4 yv[kDotBatch][E / 4];
 #pragma unroll
-                for (int e = 0; e < E; ++e) acc = fmaf(w[e], y[e0 + e], acc);
+                for (int k = 0; k < kDotBatch; ++k) {
+                    const int v = min(v0 + k * kWave, nvec - 1);  // clamped; unused past the end
+                    wv[k] = *reinterpret_cast<const Vec16*>(W + (size_t)v * E);
+#pragma unroll
+                    for (int q = 0; q < E / 4; ++q)
+                        yv[k][q] = *reinterpret_cast<const float4*>(y + (size_t)v * E + 4 * q);
+                }
+                // branch-free: a vector past the end (a clamped load) gets zero inputs and
+                // adds exact zeros (weights are finite), so the loads stay together
+#pragma unroll
+                for (int k = 0; k < kDotBatch; ++k) {
+                    const bool ok = v0 + k * kWave < nvec;
+                    float w[E];
+                    unpack<T>(wv[k], w);
+#pragma unroll
+                    for (int q = 0; q < E / 4; ++q) {
+                        acc = fmaf(w[4 * q + 0], ok ? yv[k][q].x : 0.f, acc);
+                        acc = fmaf(w[4 * q + 1], ok ? yv[k][q].y : 0.f, acc);
+                        acc = fmaf(w[4 * q + 2], ok ? yv[k][q].z : 0.f, acc);
+                        acc = fmaf(w[4 * q + 3], ok ? yv[k][q].w : 0.f, acc);
+                    }
+                }
             }
             acc = wave_sum(acc);
             if (lane == 0) cache[(((size_t)b * a.h + i) * a.n_cap + p) * a.dh + c] = to_store<T>(acc);

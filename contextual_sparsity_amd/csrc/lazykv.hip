@@ -11,7 +11,8 @@
 //   block B:            kv_next[i] = n + 1 for the selected heads, kv_prev[i] otherwise;
 //   the other blocks:   for each selected head i and each position p in [kv_prev[i], n),
 //                       K[b, i, p] = W_i^K Y[b, p] and V[b, i, p] = W_i^V Y[b, p], rounded
-//                       to the cache type; a wave per output row (K or V column c).
+//                       to the cache type; a block per four output rows (K or V columns),
+//                       its waves taking every fourth position, two per pass.
 // kv_len holds two buffers of h entries read and written alternately by the parity of n,
 // so no block reads an entry that another block of the same launch writes.
 #include "gemv.hpp"
@@ -21,9 +22,11 @@ namespace djv {
 namespace {
 
 constexpr int kLazyThreads = 256;
-constexpr int kLazyRows = kLazyThreads / kWave;  // output rows per block (a wave each)
+constexpr int kLazyRows = kLazyThreads / kWave;  // waves per block: position phases of a row tile
 constexpr int kSaveBatch = 16;  // values of the saved input per thread in flight
-constexpr int kDotBatch = 8;    // 16-byte weight vectors (and their inputs) per lane in flight
+constexpr int kDotBatch = 4;    // 16-byte weight vectors (and their inputs) per lane in flight
+constexpr int kRowTile = 4;     // output rows per catch-up wave
+constexpr int kPosTile = 2;     // positions per catch-up pass
 
 template <typename T>
 __global__ __launch_bounds__(kLazyThreads) void lazy_kv_kernel(LazyKvArgs a) {
@@ -63,55 +66,81 @@ __global__ __launch_bounds__(kLazyThreads) void lazy_kv_kernel(LazyKvArgs a) {
         }
         return;
     }
-    // catch-up: output row j of head slot u (j < dh: K column j, else V column j - dh)
-    const int rows_per_head = 2 * a.dh;
-    const int g = (bid - a.B - 1) * kLazyRows + wv;
-    const int u = g / rows_per_head, j = g - u * rows_per_head;
+    // catch-up: block g owns kRowTile consecutive output rows j0 .. j0+3 of head slot u
+    // (j < dh: K column j, else V column j - dh; a tile never straddles the two since
+    // dh % 4 == 0), and its wave w the positions start + w, start + w + 4, ..., kPosTile of
+    // them per pass: each weight vector serves kPosTile positions and each input vector
+    // kRowTile rows, and the four waves walk a head's skipped positions side by side.
+    const int tiles_per_head = 2 * a.dh / kRowTile;
+    const int g = bid - a.B - 1;
+    const int u = g / tiles_per_head, j0 = (g - u * tiles_per_head) * kRowTile;
     if (u >= count) return;  // uniform over the wave
     const int i = unit_of(a.heads, u, a.flags);
     if (i < 0) return;
-    const int part = 1 + j / a.dh, c = j % a.dh;
+    const int part = 1 + j0 / a.dh, c0 = j0 % a.dh;
     const int start = max(a.kv_prev[i], 0);
     if (start >= a.n) return;
     constexpr int E = WTraits<T>::kPerVec;
-    const T* W = reinterpret_cast<const T*>(a.Wqkv) + (((size_t)i * 3 + part) * a.dh + c) * a.d;
+    const T* W = reinterpret_cast<const T*>(a.Wqkv) + (((size_t)i * 3 + part) * a.dh + c0) * a.d;
     T* cache = reinterpret_cast<T*>(part == 1 ? a.Kc : a.Vc);
     const int nvec = a.d / E;  // 16-byte weight vectors per row (d % 8 == 0)
-    for (int p = start; p < a.n; ++p) {
+    for (int p0 = start + wv; p0 < a.n; p0 += kLazyRows * kPosTile) {
         for (int b = 0; b < a.B; ++b) {
-            const float* y = a.Y + ((size_t)b * a.n_cap + p) * a.d;
-            // lane's vectors v = lane, lane + 64, ... in order, kDotBatch of them (weights
-            // and inputs) requested before the first multiply
-            float acc = 0.f;
+            const float* yb = a.Y + (size_t)b * a.n_cap * a.d;
+            // per (row, position): the lane's vectors v = lane, lane + 64, ... in order,
+            // kDotBatch of them (weights and inputs) requested before the first multiply
+            float acc[kRowTile][kPosTile];
+#pragma unroll
+            for (int r = 0; r < kRowTile; ++r)
+#pragma unroll
+                for (int t = 0; t < kPosTile; ++t) acc[r][t] = 0.f;
             for (int v0 = lane; v0 < nvec; v0 += kWave * kDotBatch) {
-                Vec16 wv[kDotBatch];
-                float4 yv[kDotBatch][E / 4];
+                Vec16 wv[kRowTile][kDotBatch];
+                float4 yv[kPosTile][kDotBatch][E / 4];
 #pragma unroll
                 for (int k = 0; k < kDotBatch; ++k) {
                     const int v = min(v0 + k * kWave, nvec - 1);  // clamped; unused past the end
-                    wv[k] = *reinterpret_cast<const Vec16*>(W + (size_t)v * E);
 #pragma unroll
-                    for (int q = 0; q < E / 4; ++q)
-                        yv[k][q] = *reinterpret_cast<const float4*>(y + (size_t)v * E + 4 * q);
+                    for (int r = 0; r < kRowTile; ++r)
+                        wv[r][k] = *reinterpret_cast<const Vec16*>(W + (size_t)r * a.d + (size_t)v * E);
+#pragma unroll
+                    for (int t = 0; t < kPosTile; ++t) {
+                        const int p = min(p0 + t * kLazyRows, a.n - 1);  // clamped; not stored past n
+                        const float* y = yb + (size_t)p * a.d + (size_t)v * E;
+#pragma unroll
+                        for (int q = 0; q < E / 4; ++q) yv[t][k][q] = *reinterpret_cast<const float4*>(y + 4 * q);
+                    }
                 }
                 // branch-free: a vector past the end (a clamped load) gets zero inputs and
                 // adds exact zeros (weights are finite), so the loads stay together
 #pragma unroll
                 for (int k = 0; k < kDotBatch; ++k) {
                     const bool ok = v0 + k * kWave < nvec;
-                    float w[E];
-                    unpack<T>(wv[k], w);
 #pragma unroll
-                    for (int q = 0; q < E / 4; ++q) {
-                        acc = fmaf(w[4 * q + 0], ok ? yv[k][q].x : 0.f, acc);
-                        acc = fmaf(w[4 * q + 1], ok ? yv[k][q].y : 0.f, acc);
-                        acc = fmaf(w[4 * q + 2], ok ? yv[k][q].z : 0.f, acc);
-                        acc = fmaf(w[4 * q + 3], ok ? yv[k][q].w : 0.f, acc);
+                    for (int r = 0; r < kRowTile; ++r) {
+                        float w[E];
+                        unpack<T>(wv[r][k], w);
+#pragma unroll
+                        for (int t = 0; t < kPosTile; ++t)
+#pragma unroll
+                            for (int q = 0; q < E / 4; ++q) {
+                                acc[r][t] = fmaf(w[4 * q + 0], ok ? yv[t][k][q].x : 0.f, acc[r][t]);
+                                acc[r][t] = fmaf(w[4 * q + 1], ok ? yv[t][k][q].y : 0.f, acc[r][t]);
+                                acc[r][t] = fmaf(w[4 * q + 2], ok ? yv[t][k][q].z : 0.f, acc[r][t]);
+                                acc[r][t] = fmaf(w[4 * q + 3], ok ? yv[t][k][q].w : 0.f, acc[r][t]);
+                            }
                     }
                 }
             }
-            acc = wave_sum(acc);
-            if (lane == 0) cache[(((size_t)b * a.h + i) * a.n_cap + p) * a.dh + c] = to_store<T>(acc);
+#pragma unroll
+            for (int r = 0; r < kRowTile; ++r)
+#pragma unroll
+                for (int t = 0; t < kPosTile; ++t) {
+                    const float v = wave_sum(acc[r][t]);
+                    const int p = p0 + t * kLazyRows;
+                    if (lane == 0 && p < a.n)
+                        cache[(((size_t)b * a.h + i) * a.n_cap + p) * a.dh + c0 + r] = to_store<T>(v);
+                }
         }
     }
 }
@@ -121,8 +150,8 @@ __global__ __launch_bounds__(kLazyThreads) void lazy_kv_kernel(LazyKvArgs a) {
 hipError_t launch_lazy_kv(bool f16, const LazyKvArgs& a, hipStream_t s) {
     if (a.B < 1 || a.d < 1 || a.h < 1 || a.n < 0 || a.n >= a.n_cap || a.heads.cap < 1)
         return hipErrorInvalidValue;
-    const long long rows = (long long)a.heads.cap * 2 * a.dh;
-    const dim3 grid((unsigned)(a.B + 1 + (rows + kLazyRows - 1) / kLazyRows));
+    const long long tiles = (long long)a.heads.cap * 2 * a.dh / kRowTile;  // dh % 4 == 0
+    const dim3 grid((unsigned)(a.B + 1 + tiles));
     if (f16)
         hipLaunchKernelGGL(lazy_kv_kernel<__half>, grid, dim3(kLazyThreads), 0, s, a);
     else

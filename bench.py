@@ -606,6 +606,21 @@ def main(argv=None) -> int:
     ms_step, wall_ms = timed(args.steps)
     log(f"sparse step {ms_step:.3f} ms (wall {wall_ms:.3f} ms)")
 
+    # spread of single steps (a separate pass after the timed region): each step between
+    # its own pair of events on the main stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record(s_main)
+        step()
+        b.record(s_main)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in evs)
+    pick = lambda q: per[min(len(per) - 1, int(round(q * (len(per) - 1))))]
+    step_spread = {"median_ms": round(pick(0.5), 4), "p10_ms": round(pick(0.1), 4),
+                   "p90_ms": round(pick(0.9), 4), "steps": len(per)}
+
     def family_time(fam, n_steps):
         cap = n_steps * L + 4
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * cap)]
@@ -750,6 +765,7 @@ def main(argv=None) -> int:
         "tokens_per_s": round(1e3 / ms_step, 1),
         "bytes_per_layer": lb,
         "wall_ms_per_step": round(wall_ms, 4),
+        "step_spread": step_spread,
         "dense": dense,
         "speedup_vs_dense": round(dense["ms_per_step"] / ms_step, 3) if dense else None,
         "roofline": {"kernel": "Q/K/V of the kept heads + next layer's predictor first layers "

@@ -103,6 +103,13 @@ def parse(argv=None):
     return ap.parse_args(argv)
 
 
+def device_facts(torch) -> dict:
+    """What the run measured on: name, architecture, compute units, HBM capacity."""
+    pr = torch.cuda.get_device_properties(0)
+    return {"name": pr.name, "arch": getattr(pr, "gcnArchName", ""), "compute_units": pr.multi_processor_count,
+            "hbm_GiB": round(pr.total_memory / 2**30, 1)}
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -766,6 +773,7 @@ def main(argv=None) -> int:
         "bytes_per_layer": lb,
         "wall_ms_per_step": round(wall_ms, 4),
         "step_spread": step_spread,
+        "device": device_facts(torch),
         "dense": dense,
         "speedup_vs_dense": round(dense["ms_per_step"] / ms_step, 3) if dense else None,
         "roofline": {"kernel": "Q/K/V of the kept heads + next layer's predictor first layers "

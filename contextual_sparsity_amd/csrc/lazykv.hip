@@ -24,9 +24,9 @@ namespace {
 constexpr int kLazyThreads = 256;
 constexpr int kLazyRows = kLazyThreads / kWave;  // waves per block: position phases of a row tile
 constexpr int kSaveBatch = 16;  // values of the saved input per thread in flight
-constexpr int kDotBatch = 4;    // 16-byte weight vectors (and their inputs) per lane in flight
-constexpr int kRowTile = 4;     // output rows per catch-up wave
-constexpr int kPosTile = 2;     // positions per catch-up pass
+constexpr int kRowTile = 4;     // output rows per catch-up block
+constexpr int kPosTile = 2;     // positions per catch-up wave and pass
+constexpr int kChunkVec = 256;  // weight vectors per row staged in LDS at a time (16 KiB per tile)
 
 template <typename T>
 __global__ __launch_bounds__(kLazyThreads) void lazy_kv_kernel(LazyKvArgs a) {
@@ -70,56 +70,75 @@ __global__ __launch_bounds__(kLazyThreads) void lazy_kv_kernel(LazyKvArgs a) {
     // (j < dh: K column j, else V column j - dh; a tile never straddles the two since
     // dh % 4 == 0), and its wave w the positions start + w, start + w + 4, ..., kPosTile of
     // them per pass: each weight vector serves kPosTile positions and each input vector
-    // kRowTile rows, and the four waves walk a head's skipped positions side by side.
+    // kRowTile rows, and the four waves walk a head's skipped positions side by side.  The
+    // tile's weights pass through LDS in chunks of kChunkVec vectors per row, each chunk read
+    // from memory once for all four waves.  Every test before the first barrier depends
+    // only on the block's tile, so the block takes the same path throughout.
+    __shared__ Vec16 wsh[kRowTile][kChunkVec];
     const int tiles_per_head = 2 * a.dh / kRowTile;
     const int g = bid - a.B - 1;
     const int u = g / tiles_per_head, j0 = (g - u * tiles_per_head) * kRowTile;
-    if (u >= count) return;  // uniform over the wave
+    if (u >= count) return;  // uniform over the block
     const int i = unit_of(a.heads, u, a.flags);
     if (i < 0) return;
     const int part = 1 + j0 / a.dh, c0 = j0 % a.dh;
     const int start = max(a.kv_prev[i], 0);
     if (start >= a.n) return;
     constexpr int E = WTraits<T>::kPerVec;
-    const T* W = reinterpret_cast<const T*>(a.Wqkv) + (((size_t)i * 3 + part) * a.dh + c0) * a.d;
+    const Vec16* W = reinterpret_cast<const Vec16*>(reinterpret_cast<const T*>(a.Wqkv) +
+                                                    (((size_t)i * 3 + part) * a.dh + c0) * a.d);
     T* cache = reinterpret_cast<T*>(part == 1 ? a.Kc : a.Vc);
     const int nvec = a.d / E;  // 16-byte weight vectors per row (d % 8 == 0)
-    for (int p0 = start + wv; p0 < a.n; p0 += kLazyRows * kPosTile) {
+    const int passes = (a.n - start + kLazyRows * kPosTile - 1) / (kLazyRows * kPosTile);
+    constexpr int kLaneVec = kChunkVec / kWave;  // a lane's vectors of a chunk, per row
+    for (int ps = 0; ps < passes; ++ps) {
+        const int p0 = start + wv + ps * kLazyRows * kPosTile;  // positions p0 + 4t
         for (int b = 0; b < a.B; ++b) {
             const float* yb = a.Y + (size_t)b * a.n_cap * a.d;
-            // per (row, position): the lane's vectors v = lane, lane + 64, ... in order,
-            // kDotBatch of them (weights and inputs) requested before the first multiply
+            // per (row, position): the lane's vectors v = lane, lane + 64, ... in order
             float acc[kRowTile][kPosTile];
 #pragma unroll
             for (int r = 0; r < kRowTile; ++r)
 #pragma unroll
                 for (int t = 0; t < kPosTile; ++t) acc[r][t] = 0.f;
-            for (int v0 = lane; v0 < nvec; v0 += kWave * kDotBatch) {
-                Vec16 wv[kRowTile][kDotBatch];
-                float4 yv[kPosTile][kDotBatch][E / 4];
+            for (int cv = 0; cv < nvec; cv += kChunkVec) {
+                __syncthreads();  // the previous chunk's readers are done
+                {
+                    Vec16 st[kRowTile * kChunkVec / kLazyThreads];
 #pragma unroll
-                for (int k = 0; k < kDotBatch; ++k) {
-                    const int v = min(v0 + k * kWave, nvec - 1);  // clamped; unused past the end
+                    for (int k = 0; k < kRowTile * kChunkVec / kLazyThreads; ++k) {
+                        const int e = tid + k * kLazyThreads, r = e / kChunkVec, v = e - r * kChunkVec;
+                        st[k] = W[(size_t)r * nvec + min(cv + v, nvec - 1)];  // clamped; unused past the end
+                    }
 #pragma unroll
-                    for (int r = 0; r < kRowTile; ++r)
-                        wv[r][k] = *reinterpret_cast<const Vec16*>(W + (size_t)r * a.d + (size_t)v * E);
+                    for (int k = 0; k < kRowTile * kChunkVec / kLazyThreads; ++k) {
+                        const int e = tid + k * kLazyThreads, r = e / kChunkVec, v = e - r * kChunkVec;
+                        wsh[r][v] = st[k];
+                    }
+                }
+                // this wave's inputs of the chunk while the stage completes
+                float4 yv[kPosTile][kLaneVec][E / 4];
 #pragma unroll
-                    for (int t = 0; t < kPosTile; ++t) {
-                        const int p = min(p0 + t * kLazyRows, a.n - 1);  // clamped; not stored past n
+                for (int t = 0; t < kPosTile; ++t) {
+                    const int p = min(p0 + t * kLazyRows, a.n - 1);  // clamped; not stored past n
+#pragma unroll
+                    for (int k = 0; k < kLaneVec; ++k) {
+                        const int v = min(cv + lane + k * kWave, nvec - 1);
                         const float* y = yb + (size_t)p * a.d + (size_t)v * E;
 #pragma unroll
                         for (int q = 0; q < E / 4; ++q) yv[t][k][q] = *reinterpret_cast<const float4*>(y + 4 * q);
                     }
                 }
-                // branch-free: a vector past the end (a clamped load) gets zero inputs and
-                // adds exact zeros (weights are finite), so the loads stay together
+                __syncthreads();
+                // branch-free: a vector past the end gets zero inputs and adds exact zeros
+                // (weights are finite)
 #pragma unroll
-                for (int k = 0; k < kDotBatch; ++k) {
-                    const bool ok = v0 + k * kWave < nvec;
+                for (int k = 0; k < kLaneVec; ++k) {
+                    const bool ok = cv + lane + k * kWave < nvec;
 #pragma unroll
                     for (int r = 0; r < kRowTile; ++r) {
                         float w[E];
-                        unpack<T>(wv[r][k], w);
+                        unpack<T>(wsh[r][lane + k * kWave], w);
 #pragma unroll
                         for (int t = 0; t < kPosTile; ++t)
 #pragma unroll

@@ -105,6 +105,24 @@ def test_lazy_kv_batches_and_threshold(B, mode):
     _check(shape, w, K0, V0, steps, L)
 
 
+# the recompute stages weight rows through LDS in chunks of 256 16-byte vectors: fp32 rows
+# of 1200 (300 vectors: a full chunk and a ragged one, d_h 64) and fp16 rows of 4104 (513
+# vectors: two full chunks and one vector)
+@pytest.mark.parametrize("shape", [
+    synth.LayerShape(d=1200, N=1200, h=8, dh=64, n=200, r=128, dtype="f32"),
+    synth.LayerShape(d=4104, N=2000, h=6, dh=128, n=150, r=128, dtype="f16"),
+], ids=["f32-d1200-dh64", "f16-d4104"])
+def test_lazy_kv_weight_chunks(shape):
+    print(f"lazy K/V {shape.dtype} d={shape.d} dh={shape.dh}", flush=True)
+    L, T = 2, 6
+    shape, w, K0, V0, steps = _run_steps(shape, L, T, 53, lazy=True, lookahead=True)
+    _check(shape, w, K0, V0, steps, L)
+    sets = [[set(st["sets_A"][l, : int(st["counts"][l, 0])].tolist()) for st in steps]
+            for l in range(L)]
+    assert any(i in sets[l][t] and i not in sets[l][t - 1] for l in range(L) for t in range(1, T)
+               for i in range(shape.h))
+
+
 def test_without_lazy_kv_a_reselected_head_reads_stale_entries():
     # the same steps without lazy K/V: a head that skipped a step attends over the cache's
     # old contents at that position, which differ from the all-heads cache

@@ -6,8 +6,9 @@ Checks per layer:
     identical scores), the GPU scores match the oracle's scores of the same input, and
     the sets are valid top-k sets of the oracle's scores within twice the score gap;
   * x' (after attention) and the layer output match the oracle to the dtype tolerance.
-Also the full-size workloads: one OPT-125m layer (fp32), one OPT-175B-shaped layer,
-a 3-layer OPT-6.7B-shaped lookahead stack, one OPT-66B-shaped layer at batch 1 and 4."""
+Also the full-size workloads: one OPT-125m layer (fp32), one OPT-175B-shaped layer and a
+2-layer OPT-175B-shaped lookahead stack (the benchmark's launch configuration), a 3-layer
+OPT-6.7B-shaped lookahead stack, one OPT-66B-shaped layer at batch 1 and 4."""
 import numpy as np
 import pytest
 import torch
@@ -232,6 +233,17 @@ def test_opt175b_layer():
     assert (st.k_A, st.k_M) == (20, 2458)
     x, tr = st.run(lookahead=False, single_layer=True)
     check_stack(st, host(x), tr, lookahead=False)
+
+
+@pytest.mark.slow
+def test_opt175b_lookahead_stack():
+    # the benchmark's launch configuration (lookahead stack, fused launches) at its full
+    # layer shape, two layers
+    print("opt175b 2-layer lookahead", flush=True)
+    wl, st = _workload_stack("opt175b-24layers-fp16", L=2)
+    assert (st.k_A, st.k_M) == (20, 2458)
+    x, tr = st.run(lookahead=True)
+    check_stack(st, host(x), tr, lookahead=True)
 
 
 @pytest.mark.slow

@@ -33,6 +33,7 @@ constexpr int kThreads = 256;
 __device__ __forceinline__ int chunk_rows(const AxpyArgs& a, int rows) {
     const int rows_cap = a.list.cap * a.rpu;
     const int nch_cap = (rows_cap + a.rows_per_chunk - 1) / a.rows_per_chunk;
+    if (nch_cap == 0) return a.rows_per_chunk;  // an empty list (top-k with k = 0): no chunk
     int r = (rows + nch_cap - 1) / nch_cap;
     r = (r + a.chunk_step - 1) / a.chunk_step * a.chunk_step;
     return min(max(r, a.chunk_step), a.rows_per_chunk);

@@ -24,6 +24,26 @@ def rel_l2(got, ref) -> float:
     return float(np.linalg.norm(g - r) / (den if den > 0 else 1.0))
 
 
+# An element may differ from the reference by at most this many tolerances times the
+# reference's root-mean-square value, so that a single wrong element (a misplaced column
+# or row) fails even where the whole-vector relative L2 error would stay small.
+ELEMENT_FACTOR = 10.0
+
+
+def assert_close(got, ref, tol: float, ctx=None) -> None:
+    """Relative L2 error below tol, and every element within ELEMENT_FACTOR * tol * rms(ref)."""
+    g = np.asarray(got, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape, (ctx, g.shape, r.shape)
+    e = rel_l2(g, r)
+    assert e < tol, (ctx, "rel L2", e)
+    if r.size:
+        rms = float(np.sqrt(np.mean(r * r)))
+        worst = float(np.abs(g - r).max())
+        assert worst <= ELEMENT_FACTOR * tol * (rms if rms > 0 else 1.0), \
+            (ctx, "element", worst, "rms", rms, "at", np.unravel_index(int(np.abs(g - r).argmax()), g.shape))
+
+
 def host(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().numpy()
 
@@ -66,3 +86,12 @@ def check_sets_valid(sel_gpu, z_oracle, k: int, delta: float) -> None:
     mask = np.zeros(len(z), dtype=bool)
     mask[S] = True
     assert z[mask].min() >= z[~mask].max() - 2 * delta - 1e-30, (z[mask].min(), z[~mask].max(), delta)
+
+
+def check_threshold_valid(sel_gpu, z_oracle, tau: float, delta: float) -> None:
+    """A threshold set chosen from slightly different scores is valid when it holds every
+    unit whose oracle score is above tau + delta and none below tau - delta."""
+    z = np.asarray(z_oracle, dtype=np.float64)
+    mask = np.zeros(len(z), dtype=bool)
+    mask[np.asarray(sel_gpu, dtype=np.int64)] = True
+    assert mask[z > tau + delta].all() and not mask[z < tau - delta].any(), (tau, delta)

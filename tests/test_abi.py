@@ -45,6 +45,11 @@ def test_workspace_sizes():
     m = dj.make_model(dj.DJV_F16, 1, 12288, 49152, 96, 128, 1024, 2048, 2049, 128 ** -0.5,
                       dj.DJV_TOPK, 20, 2458)
     assert 0 < dj.dejavu_workspace_bytes_model(m) <= big
+    # top-k with k = 0 (an empty list of capacity 0) is a valid model
+    for k_A, k_M in ((0, 0), (0, 2458), (20, 0)):
+        m0 = dj.make_model(dj.DJV_F16, 1, 12288, 49152, 96, 128, 1024, 2048, 2049, 128 ** -0.5,
+                           dj.DJV_TOPK, k_A, k_M)
+        assert 0 < dj.dejavu_workspace_bytes_model(m0) <= big
     with pytest.raises(dj.DejavuError) as e:
         dj.dejavu_workspace_bytes(-1)
     assert e.value.status == dj.DJV_EINVAL

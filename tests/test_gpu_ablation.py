@@ -9,7 +9,7 @@ import torch
 import oracle as O
 from contextual_sparsity_amd import dejavu as dj
 from contextual_sparsity_amd import synth
-from helpers import DEV, TOL, host, idx_tensor, oracle_layer, rel_l2, wt_code, ws_for
+from helpers import DEV, TOL, assert_close, host, idx_tensor, oracle_layer, rel_l2, ws_for, wt_code
 
 pytestmark = pytest.mark.gpu
 
@@ -67,4 +67,4 @@ def test_unfused_mlp_equals_fused(name, B):
     assert torch.equal(fused, unfused)
     Wn = oracle_layer(w)
     ref = O.sparse_mlp(host(y), Wn.W1, Wn.b1, Wn.W2, S)
-    assert rel_l2(host(unfused) - host(x), ref) < TOL[s.dtype]
+    assert_close(host(unfused) - host(x), ref, TOL[s.dtype])

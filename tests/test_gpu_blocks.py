@@ -8,7 +8,7 @@ import torch
 import oracle as O
 from contextual_sparsity_amd import dejavu as dj
 from contextual_sparsity_amd import synth
-from helpers import DEV, TOL, host, idx_tensor, oracle_layer, rel_l2, wt_code, ws_for
+from helpers import DEV, TOL, assert_close, host, idx_tensor, oracle_layer, rel_l2, ws_for, wt_code
 
 pytestmark = pytest.mark.gpu
 
@@ -40,7 +40,7 @@ def test_layernorm(B):
         y = torch.empty_like(x)
         dj.dejavu_layernorm(B, d, x, y, 1e-5)
         torch.cuda.synchronize()
-        assert rel_l2(host(y), O.layernorm(host(x))) < 1e-6
+        assert_close(host(y), O.layernorm(host(x)), 1e-6)
     # in place, and a constant row
     x = torch.full((1, 1024), 3.0, device=DEV)
     dj.dejavu_layernorm(1, 1024, x, x, 1e-5)
@@ -63,7 +63,7 @@ def test_predict(name, B):
         dj.dejavu_predict(wt_code(s), B, s.d, s.r, n_out, y, P1, P2, dj.DJV_TOPK, k, 0.5, idx, cnt, z, ws)
         torch.cuda.synchronize()
         z_ref = O.predictor_logits_f64(host(y), host(P1), host(P2))
-        assert rel_l2(host(z), z_ref) < TOL[s.dtype]
+        assert_close(host(z), z_ref, TOL[s.dtype])
         got = host(idx)[: int(cnt.item())]
         # bit-exact on identical scores
         assert np.array_equal(got, O.select(host(z), O.TOPK, k=k))
@@ -96,13 +96,13 @@ def test_sparse_mlp(name, B):
                              None, out, ws)
         torch.cuda.synchronize()
         ref = O.sparse_mlp(host(y), Wn.W1, Wn.b1, Wn.W2, S)
-        assert rel_l2(host(out), ref) < TOL[s.dtype], (k, rel_l2(host(out), ref))
+        assert_close(host(out), ref, TOL[s.dtype], (k, rel_l2(host(out), ref)))
         # with the residual, in place
         out2 = x.clone()
         dj.dejavu_sparse_mlp(wt_code(s), B, s.d, s.N, y, w["W1"], w["b1"], w["W2"], idx, cnt, cap,
                              out2, out2, ws)
         torch.cuda.synchronize()
-        assert rel_l2(host(out2) - host(x), ref) < TOL[s.dtype]
+        assert_close(host(out2) - host(x), ref, TOL[s.dtype])
 
 
 @pytest.mark.parametrize("name", list(SHAPES))
@@ -114,7 +114,7 @@ def test_dense_mlp(name):
     torch.cuda.synchronize()
     Wn = oracle_layer(w)
     ref = O.dense_mlp(host(y), Wn.W1, Wn.b1, Wn.W2)
-    assert rel_l2(host(out) - host(x), ref) < TOL[s.dtype]
+    assert_close(host(out) - host(x), ref, TOL[s.dtype])
 
 
 def test_sparse_mlp_count_below_capacity_and_bad_index():
@@ -130,20 +130,20 @@ def test_sparse_mlp_count_below_capacity_and_bad_index():
     dj.dejavu_poll_device_error()
     dj.dejavu_sparse_mlp(wt_code(s), 1, s.d, s.N, y, w["W1"], w["b1"], w["W2"], idx, cnt, 100, None, out, ws)
     assert dj.dejavu_poll_device_error() == 0
-    assert rel_l2(host(out), O.sparse_mlp(host(y), Wn.W1, Wn.b1, Wn.W2, S)) < 1e-2
+    assert_close(host(out), O.sparse_mlp(host(y), Wn.W1, Wn.b1, Wn.W2, S), 1e-2)
     # an index past N contributes nothing and raises the device flag
     idx[5] = s.N + 11
     dj.dejavu_sparse_mlp(wt_code(s), 1, s.d, s.N, y, w["W1"], w["b1"], w["W2"], idx, cnt, 100, None, out, ws)
     assert dj.dejavu_poll_device_error() & dj.DJV_FLAG_BAD_INDEX
     S2 = np.delete(S, 5)
-    assert rel_l2(host(out), O.sparse_mlp(host(y), Wn.W1, Wn.b1, Wn.W2, S2)) < 1e-2
+    assert_close(host(out), O.sparse_mlp(host(y), Wn.W1, Wn.b1, Wn.W2, S2), 1e-2)
     # a count above the capacity is clamped and flagged
     idx[5] = int(S[5])
     cnt.fill_(1000)
     dj.dejavu_sparse_mlp(wt_code(s), 1, s.d, s.N, y, w["W1"], w["b1"], w["W2"], idx[:40].clone(), cnt, 40,
                          None, out, ws)
     assert dj.dejavu_poll_device_error() & dj.DJV_FLAG_BAD_COUNT
-    assert rel_l2(host(out), O.sparse_mlp(host(y), Wn.W1, Wn.b1, Wn.W2, S)) < 1e-2
+    assert_close(host(out), O.sparse_mlp(host(y), Wn.W1, Wn.b1, Wn.W2, S), 1e-2)
     # count 0: out = resid
     cnt.fill_(0)
     dj.dejavu_sparse_mlp(wt_code(s), 1, s.d, s.N, y, w["W1"], w["b1"], w["W2"], idx, cnt, 100, x, out, ws)
@@ -172,11 +172,11 @@ def test_sparse_mha(name, B):
     for S in ([0], [1, s.h - 1], list(range(0, s.h, 2)), list(range(s.h))):
         S = np.array(S, dtype=np.int32)
         out, ref, kn, vn, K0, V0 = _mha_case(s, w, x, S, s.dh ** -0.5)
-        assert rel_l2(host(out), ref) < TOL[s.dtype], (S, rel_l2(host(out), ref))
+        assert_close(host(out), ref, TOL[s.dtype], (S, rel_l2(host(out), ref)))
         K1, V1 = host(w["K"]), host(w["V"])
         for slot, i in enumerate(S):
-            assert rel_l2(K1[:, i, s.n], kn[:, slot]) < TOL[s.dtype]
-            assert rel_l2(V1[:, i, s.n], vn[:, slot]) < TOL[s.dtype]
+            assert_close(K1[:, i, s.n], kn[:, slot], TOL[s.dtype])
+            assert_close(V1[:, i, s.n], vn[:, slot], TOL[s.dtype])
         # other heads' position n and every other position are untouched
         mask = np.ones(s.h, dtype=bool)
         mask[S] = False
@@ -190,10 +190,10 @@ def test_sparse_mha_edge_lengths(name):
     S = np.array([2, 3], dtype=np.int32)
     for n in (0, 1, 127, 128, 129, 255, 256):
         out, ref, *_ = _mha_case(s, w, x, S, 1.0 / 8, n=n)
-        assert rel_l2(host(out), ref) < TOL[s.dtype], n
+        assert_close(host(out), ref, TOL[s.dtype], n)
     # the literal formula (scale 1)
     out, ref, *_ = _mha_case(s, w, x, S, 1.0)
-    assert rel_l2(host(out), ref) < TOL[s.dtype]
+    assert_close(host(out), ref, TOL[s.dtype])
 
 
 @pytest.mark.parametrize("name", list(SHAPES))
@@ -206,8 +206,8 @@ def test_dense_mha(name):
                         s.dh ** -0.5, x, out, ws_for(s))
     torch.cuda.synchronize()
     ref, kn, vn = O.dense_mha(host(y), host(w["Wqkv"]), host(w["Wo"]), K0, V0, s.n, s.dh ** -0.5)
-    assert rel_l2(host(out) - host(x), ref) < TOL[s.dtype]
-    assert rel_l2(host(w["K"])[:, :, s.n], kn) < TOL[s.dtype]
+    assert_close(host(out) - host(x), ref, TOL[s.dtype])
+    assert_close(host(w["K"])[:, :, s.n], kn, TOL[s.dtype])
 
 
 def test_blocks_deterministic():

@@ -14,7 +14,7 @@ import torch
 import oracle as O
 from contextual_sparsity_amd import dejavu as dj
 from contextual_sparsity_amd import synth
-from helpers import DEV, TOL, host, rel_l2, wt_code
+from helpers import DEV, TOL, assert_close, host, rel_l2, wt_code
 
 pytestmark = pytest.mark.gpu
 
@@ -76,8 +76,8 @@ def _check(shape, w, K0, V0, steps, L):
             hi = int(kv_len[i])
             assert n0 <= hi <= n_end
             if hi > n0:
-                assert rel_l2(Kg[:, i, n0:hi], K[:, i, n0:hi]) < tol, (l, i)
-                assert rel_l2(Vg[:, i, n0:hi], V[:, i, n0:hi]) < tol, (l, i)
+                assert_close(Kg[:, i, n0:hi], K[:, i, n0:hi], tol, (l, i))
+                assert_close(Vg[:, i, n0:hi], V[:, i, n0:hi], tol, (l, i))
 
 
 SMALL = synth.LayerShape(d=1032, N=1500, h=6, dh=128, n=300, r=136, dtype="f16")

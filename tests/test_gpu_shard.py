@@ -17,7 +17,7 @@ import oracle as O
 from contextual_sparsity_amd import configs
 from contextual_sparsity_amd import dejavu as dj
 from contextual_sparsity_amd import synth
-from helpers import DEV, TOL, host, rel_l2, wt_code, ws_for
+from helpers import DEV, TOL, assert_close, host, rel_l2, ws_for, wt_code
 from test_gpu_layer import Stack, check_stack
 
 pytestmark = pytest.mark.gpu
@@ -137,8 +137,8 @@ def test_shard_blocks_sum_to_unsharded_block(B):
             att_sum += a
             mlp_sum += m
         torch.cuda.synchronize()
-        assert rel_l2(host(att_sum), host(att_full)) < TOL[s.dtype], g
-        assert rel_l2(host(mlp_sum), host(mlp_full)) < TOL[s.dtype], g
+        assert_close(host(att_sum), host(att_full), TOL[s.dtype], g)
+        assert_close(host(mlp_sum), host(mlp_full), TOL[s.dtype], g)
 
 
 @pytest.mark.slow

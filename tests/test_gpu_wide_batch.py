@@ -15,7 +15,7 @@ import torch
 import oracle as O
 from contextual_sparsity_amd import dejavu as dj
 from contextual_sparsity_amd import synth
-from helpers import DEV, TOL, host, idx_tensor, oracle_layer, rel_l2, wt_code, ws_for
+from helpers import DEV, TOL, assert_close, host, idx_tensor, oracle_layer, rel_l2, ws_for, wt_code
 from test_gpu_layer import Stack, check_stack
 
 pytestmark = pytest.mark.gpu
@@ -49,10 +49,10 @@ def test_predict_wide(name, B):
         dj.dejavu_predict(wt_code(s), B, s.d, s.r, n_out, y, P1, P2, dj.DJV_TOPK, k, 0.5, idx, cnt, z, ws)
         torch.cuda.synchronize()
         z_ref = O.predictor_logits_f64(host(y), host(P1), host(P2))
-        assert rel_l2(host(z), z_ref) < TOL[s.dtype], rel_l2(host(z), z_ref)
+        assert_close(host(z), z_ref, TOL[s.dtype], rel_l2(host(z), z_ref))
         # every batch row on its own, not only the whole
         for b in range(B):
-            assert rel_l2(host(z)[b], z_ref[b]) < TOL[s.dtype], b
+            assert_close(host(z)[b], z_ref[b], TOL[s.dtype], b)
         got = host(idx)[: int(cnt.item())]
         assert np.array_equal(got, O.select(host(z), O.TOPK, k=k))
 
@@ -79,9 +79,9 @@ def test_sparse_mlp_wide(name, B):
         torch.cuda.synchronize()
         ref = O.sparse_mlp(host(y), Wn.W1, Wn.b1, Wn.W2, S)
         got = host(out) - host(x)
-        assert rel_l2(got, ref) < TOL[s.dtype], (k, rel_l2(got, ref))
+        assert_close(got, ref, TOL[s.dtype], (k, rel_l2(got, ref)))
         for b in range(B):
-            assert rel_l2(got[b], ref[b]) < TOL[s.dtype], (k, b)
+            assert_close(got[b], ref[b], TOL[s.dtype], (k, b))
 
 
 @pytest.mark.parametrize("name", list(SHAPES))
@@ -100,11 +100,11 @@ def test_sparse_mha_wide(name, B):
                              w["V"], idx, cnt, cap, scale, None, out, ws_for(s))
         torch.cuda.synchronize()
         ref, kn, vn = O.sparse_mha(host(y), host(w["Wqkv"]), host(w["Wo"]), K0, V0, s.n, S, scale)
-        assert rel_l2(host(out), ref) < TOL[s.dtype], (S, rel_l2(host(out), ref))
+        assert_close(host(out), ref, TOL[s.dtype], (S, rel_l2(host(out), ref)))
         K1, V1 = host(w["K"]), host(w["V"])
         for slot, i in enumerate(S):
-            assert rel_l2(K1[:, i, s.n], kn[:, slot]) < TOL[s.dtype]
-            assert rel_l2(V1[:, i, s.n], vn[:, slot]) < TOL[s.dtype]
+            assert_close(K1[:, i, s.n], kn[:, slot], TOL[s.dtype])
+            assert_close(V1[:, i, s.n], vn[:, slot], TOL[s.dtype])
         mask = np.ones(s.h, dtype=bool)
         mask[S] = False
         assert np.array_equal(K1[:, mask], K0[:, mask]) and np.array_equal(V1[:, mask], V0[:, mask])
@@ -168,7 +168,7 @@ def test_small_batch_matrix_core_blocks(B, mfma_from_1):
     torch.cuda.synchronize()
     dj.dejavu_set_mfma_min_batch(1)
     assert not np.array_equal(outs[0], outs[1])
-    assert rel_l2(outs[0], outs[1]) < TOL[s.dtype]
+    assert_close(outs[0], outs[1], TOL[s.dtype])
 
 
 @pytest.mark.parametrize("B", [1, 3])

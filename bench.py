@@ -30,6 +30,7 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
+HEADLINE_METRIC = "sparse decode-layer µs and HBM GB/s (% of peak), OPT-175B shape, 5% MLP/20% heads"
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qkv_p1_launch_opt175b_traffic.txt")
 KERNEL_SOURCES = ["common.hpp", "gemv.hpp", "select.hpp", "attn.hpp", "gemv_f16_side.hip"]
@@ -69,13 +70,17 @@ def parse(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="opt175b-24layers-fp16")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0: the workload's)")
+    ap.add_argument("--batch", type=int, default=0, help="override the batch size (0: the workload's)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--dense-steps", type=int, default=3)
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget")
     ap.add_argument("--breakdown", action="store_true", help="time every kernel family")
-    ap.add_argument("--no-lookahead", action="store_true")
+    ap.add_argument("--no-lookahead", action="store_true", help="serial schedule for any workload")
+    ap.add_argument("--lookahead", action="store_true",
+                    help="lookahead schedule for any workload (the single-layer workloads default to "
+                         "the serial one: head set from LN(x), neuron set from LN(x'))")
     ap.add_argument("--sweep", action="store_true", help="the keep-percentage x batch sweep")
     ap.add_argument("--sweep-layers", type=int, default=8, help="distinct layers per sweep step")
     ap.add_argument("--sweep-steps", type=int, default=5)
@@ -134,58 +139,116 @@ def dense_layer_bytes(s):
 
 
 # ------------------------------------------------------------------------ CPU oracle baseline
-def cpu_baseline(wl, s, layers_gpu, preds_gpu, x0, k_A, k_M, budget_s, lb):
+def _cpu_threads_cap() -> int:
+    """Host threads the baseline may use: the CPUs this process may run on, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(wl, s, layers_gpu, preds_gpu, x0, k_A, k_M, budget_s, lb, dense_lb, lookahead=True):
+    """The float64 oracle on the host, timed on a bounded sample of the same step, in three
+    legs (numpy's BLAS pool held at one thread in each, so a leg uses exactly the threads
+    it starts):
+      * one core: the stack's layers in order (lookahead or serial sets, as on the GPU),
+        until a third of the budget;
+      * all cores: P threads (P = the host CPUs this process may use, at most 16), thread i
+        running the oracle on layer i % L' of the step from the step's input, L' = min(P, L)
+        layers held on the host (fewer threads if host memory is short); numpy releases the interpreter lock inside its array loops, so
+        the threads run in parallel.  Throughput = P layers / wall time; the effective
+        cores are the process CPU time over the wall time;
+      * dense: the dense oracle layer 0 on one core.
+    `value` is the faster leg's rate on the sparse layer's touched bytes, `cores` its threads."""
     import numpy as np
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
     host = lambda t: t.detach().cpu().numpy()
+    weights = lambda l: (O.LayerWeights(**{k: host(v) for k, v in layers_gpu[l].items()}),
+                         O.PredictorWeights(**{k: host(v) for k, v in preds_gpu[l].items()}))
     sel = O.Selection(O.TOPK, k_A=k_A, k_M=k_M)
-    x = host(x0).astype(np.float64)
-    done, t_total = 0, 0.0
-    prev_y = None
-    for l in range(len(layers_gpu)):
-        w, p = layers_gpu[l], preds_gpu[l]
-        Lw = O.LayerWeights(**{k: host(v) for k, v in w.items()})
-        Pw = O.PredictorWeights(**{k: host(v) for k, v in p.items()})
-        t0 = time.perf_counter()
-        # one layer of the lookahead stack: the sets of layer l come from LN(x_{l-1})
-        y_src = O.layernorm(x) if prev_y is None else prev_y
+    x_in = host(x0).astype(np.float64)
+
+    def sparse_one(x, Lw, Pw, y_src):
+        if not lookahead:  # head set from LN(x), neuron set from LN(x') in between
+            return O.serial_layer(x, Lw, Pw, sel, s.n, wl.scale)[0]
         S_A, S_M = O.predict_sets(y_src, Pw, sel)
-        prev_y = O.layernorm(x)
-        x, _, _, _ = O.sparse_layer(x, Lw, S_A, S_M, s.n, wl.scale)
-        t_total += time.perf_counter() - t0
-        done += 1
-        del Lw, Pw
-        if t_total >= budget_s:
-            break
-    per_layer_s = t_total / done
-    # the first layer again on one thread (numpy's BLAS pool limited to 1)
-    one_thread_s = None
-    try:
-        from threadpoolctl import threadpool_limits
-        x1 = host(x0).astype(np.float64)
-        Lw = O.LayerWeights(**{k: host(v) for k, v in layers_gpu[0].items()})
-        Pw = O.PredictorWeights(**{k: host(v) for k, v in preds_gpu[0].items()})
-        with threadpool_limits(limits=1):
+        return O.sparse_layer(x, Lw, S_A, S_M, s.n, wl.scale)[0]
+
+    with threadpool_limits(limits=1):
+        # one core: layers in order (the sets of layer l come from LN(x_{l-1})), from layer 0
+        # again after the last one while the budget lasts; small layers keep their host copy
+        x, prev_y, done, t1 = x_in, None, 0, 0.0
+        small = sum(v.numel() * v.element_size() for v in layers_gpu[0].values()) < 2**30
+        kept = {}
+        while t1 < budget_s / 3 and done < 100000:
+            l = done % len(layers_gpu)
+            Lw, Pw = kept[l] if l in kept else weights(l)
+            if small:
+                kept[l] = (Lw, Pw)
             t0 = time.perf_counter()
-            y1 = O.layernorm(x1)
-            S_A, S_M = O.predict_sets(y1, Pw, sel)
-            O.sparse_layer(x1, Lw, S_A, S_M, s.n, wl.scale)
-            one_thread_s = time.perf_counter() - t0
-        del Lw, Pw
-    except ImportError:  # pragma: no cover
-        pass
+            y_src = O.layernorm(x) if prev_y is None else prev_y
+            prev_y = O.layernorm(x)
+            x = sparse_one(x, Lw, Pw, y_src)
+            t1 += time.perf_counter() - t0
+            done += 1
+            del Lw, Pw
+        kept.clear()
+        one_us = t1 / done * 1e6
+
+        # all cores: thread i runs layer i % L, all host copies made before the clock starts
+        P = _cpu_threads_cap()
+        nl = min(P, len(layers_gpu))
+        try:
+            import psutil
+            per_layer = sum(v.numel() * v.element_size() for v in layers_gpu[0].values()) * 1.6
+            fit = int(psutil.virtual_memory().available * 0.6 // per_layer)
+            if fit < nl:
+                nl = P = max(1, fit)
+        except ImportError:  # pragma: no cover
+            pass
+        ws = [weights(l) for l in range(nl)]
+        y0 = O.layernorm(x_in)
+        reps = max(1, round(budget_s / 3 / (one_us * 1e-6) / P))  # layers per thread
+
+        def run(i):
+            for _ in range(reps):
+                sparse_one(x_in, ws[i % nl][0], ws[i % nl][1], y0)
+
+        c0, w0 = time.process_time(), time.perf_counter()
+        with ThreadPoolExecutor(P) as ex:
+            list(ex.map(run, range(P)))
+        wall = time.perf_counter() - w0
+        eff = (time.process_time() - c0) / wall
+        del ws
+        all_us = wall / (P * reps) * 1e6
+
+        # dense layer 0 on one core
+        Lw, _ = weights(0)
+        t0 = time.perf_counter()
+        O.dense_layer(x_in, Lw, s.n, wl.scale)
+        dense_us = (time.perf_counter() - t0) * 1e6
+        del Lw
+    # the faster leg is the baseline (small layers are interpreter-bound, and their threads
+    # mostly wait for one another)
+    best_us, best_p = (all_us, P) if all_us < one_us else (one_us, 1)
     return {
-        "value": round(lb / per_layer_s / 1e9, 4), "unit": "GB/s",
-        "us_per_layer": round(per_layer_s * 1e6, 1),
-        "cores": int(threads), "host_cpus": os.cpu_count(), "kind": "oracle",
-        "one_thread_us_per_layer": round(one_thread_s * 1e6, 1) if one_thread_s else None,
-        "sample": f"first {done} of {len(layers_gpu)} layers of one decode step (float64 numpy "
-                  f"oracle, lookahead sets), {t_total:.1f} s of CPU work; layer 0 again on one thread",
+        "value": round(lb / (best_us * 1e-6) / 1e9, 4), "unit": "GB/s", "kind": "oracle",
+        "cores": best_p, "cores_used": best_p, "all_cores_threads": P,
+        "all_cores_effective_cores": round(eff, 2), "host_cpus": os.cpu_count(),
+        "us_per_layer": round(best_us, 1),
+        "one_core_us_per_layer": round(one_us, 1),
+        "all_cores_us_per_layer": round(all_us, 1),
+        "dense_us_per_layer": round(dense_us, 1),
+        "dense_GBps": round(dense_lb / (dense_us * 1e-6) / 1e9, 4),
+        "sample": f"float64 numpy oracle ({'lookahead' if lookahead else 'serial'} sets), BLAS at one "
+                  f"thread per thread: {done} layers of the step in "
+                  f"order (from layer 0 again after the last) on one core ({t1:.1f} s); {P} threads at once, "
+                  f"thread i running layer i % {nl} {reps} times from the step's input ({wall:.1f} s wall, {eff:.1f} cores "
+                  f"busy on average); the dense "
+                  f"layer 0 on one core ({dense_us * 1e-6:.1f} s)",
     }
 
 
@@ -528,7 +591,7 @@ def main(argv=None) -> int:
         return 0
 
     wl = configs.WORKLOADS[args.workload]
-    s = wl.shape
+    s = wl.shape.with_(B=args.batch) if args.batch else wl.shape
     L = args.layers or wl.layers
     k_A, k_M = wl.k_A, wl.k_M
     dev = "cuda"
@@ -588,7 +651,7 @@ def main(argv=None) -> int:
     ws = dj.workspace(dj.dejavu_workspace_bytes_model(m), dev)
     x = x0.clone()
     s_main = torch.cuda.current_stream()
-    lookahead = not args.no_lookahead
+    lookahead = (wl.lookahead or args.lookahead) and not args.no_lookahead
 
     def step(dense=False):
         x.copy_(x0)
@@ -676,6 +739,17 @@ def main(argv=None) -> int:
         print(json.dumps(out), flush=True)
         return 0
     lb = layer_bytes(s, k_A, k_M)
+    unions = None
+    if s.B > 1:
+        # a batch reads the union of its tokens' sets: bytes from each layer's union sizes
+        counts = torch.zeros(L, 2, dtype=torch.int32, device=dev)
+        x.copy_(x0)
+        dj.dejavu_stack_decode(m, desc, x, lookahead, False, dj.make_trace(counts=counts), ws, s_main)
+        c = counts.cpu().tolist()
+        per = [layer_bytes(s, cA, cM) for cA, cM in c]
+        lb = {key: round(sum(p[key] for p in per) / L) for key in lb}
+        unions = {"heads_mean": round(sum(r[0] for r in c) / L, 2),
+                  "neurons_mean": round(sum(r[1] for r in c) / L, 1)}
     step_bytes = lb["total"] * L
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
 
@@ -684,7 +758,9 @@ def main(argv=None) -> int:
     # layer runs in a side block of it), timed with events around each of its launches
     e = 2 if s.dtype == "f16" else 4
     p1_bytes = 2 * s.r * s.d * e
-    k1_bytes = lb["qkv"] + p1_bytes * (L - 1) / L   # the last layer has no next layer
+    # with lookahead the launch also reads the next layer's first predictor layers (the last
+    # layer has no next layer); in the serial schedule those run in a launch of their own
+    k1_bytes = lb["qkv"] + (p1_bytes * (L - 1) / L if lookahead else 0)
 
 
     qkv_ms, qkv_n = family_time("qkv", args.steps)
@@ -744,11 +820,17 @@ def main(argv=None) -> int:
     cpu = None
     if not args.no_cpu_baseline:
         log("CPU oracle sample ...")
-        cpu = cpu_baseline(wl, s, layers, preds, x0, k_A, k_M, args.cpu_seconds, lb["total"])
-        log(f"CPU oracle {cpu['us_per_layer']} us/layer on {cpu['cores']} threads")
+        cpu = cpu_baseline(wl, s, layers, preds, x0, k_A, k_M, args.cpu_seconds, lb["total"],
+                           dense_layer_bytes(s), lookahead)
+        log(f"CPU oracle {cpu['us_per_layer']} us/layer on {cpu['cores']} threads "
+            f"({cpu['one_core_us_per_layer']} on one core; dense {cpu['dense_us_per_layer']} on one core)")
 
+    headline = wl.name == "opt175b-24layers-fp16" and s.B == 1 and L == wl.layers
+    metric = HEADLINE_METRIC if headline else (
+        f"sparse decode-layer µs and HBM GB/s (% of peak), {wl.name}{f', batch {s.B}' if s.B > 1 else ''}"
+        f"{f', {L} layers' if L != wl.layers else ''}, {wl.pct_M}% MLP/{wl.pct_A}% heads")
     out = {
-        "metric": "sparse decode-layer µs and HBM GB/s (% of peak), OPT-175B shape, 5% MLP/20% heads",
+        "metric": metric,
         "value": round(gbs, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -762,7 +844,8 @@ def main(argv=None) -> int:
         "data": "synthetic (seeded N(0,0.02) weights, N(0,0.05) predictors, N(0,1) input)",
         "config": {"workload": wl.name, "layers": L, "d": s.d, "N": s.N, "h": s.h, "dh": s.dh,
                    "n": s.n, "r": s.r, "batch": s.B, "keep_neurons_pct": wl.pct_M,
-                   "keep_heads_pct": wl.pct_A, "k_M": k_M, "k_A": k_A, "lookahead": lookahead},
+                   "keep_heads_pct": wl.pct_A, "k_M": k_M, "k_A": k_A, "lookahead": lookahead,
+                   "union_sets": unions},
         "us_per_layer": round(ms_step * 1e3 / L, 2),
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "copy_ref_GBps": round(copy_gbs, 1),
@@ -776,10 +859,11 @@ def main(argv=None) -> int:
         "device": device_facts(torch),
         "dense": dense,
         "speedup_vs_dense": round(dense["ms_per_step"] / ms_step, 3) if dense else None,
-        "roofline": {"kernel": "Q/K/V of the kept heads + next layer's predictor first layers "
-                               "(gemv_kernel, one launch per layer)", "bound": "hbm",
+        "roofline": {"kernel": ("Q/K/V of the kept heads + next layer's predictor first layers "
+                                "(gemv_kernel, one launch per layer)") if lookahead and L > 1 else
+                               "Q/K/V of the kept heads (gemv_kernel, one launch per layer)", "bound": "hbm",
                      "achieved": round(qkv_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(qkv_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                     "frac": round(qkv_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic() if headline else None,
                      "bytes_per_launch": round(k1_bytes), "us_per_launch": round(qkv_ms * 1e3, 2),
                      "launches": qkv_n},
         "kernels": kernels or None,

@@ -10,6 +10,7 @@
 #include <atomic>
 #include <cmath>
 #include <initializer_list>
+#include <mutex>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -60,6 +61,38 @@ djv_status fail(djv_status s, const char* fmt, ...) {
         hipError_t e_ = (expr);                                                            \
         if (e_ != hipSuccess) return fail(DJV_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
     } while (0)
+
+// ------------------------------------------------------------------------------------
+// Static scratch of dejavu_sparse_mlp_no_alloc, for callers that cannot allocate.  Each
+// GPU the library runs on holds its own copy of `scratch` until the process ends.  In host
+// code `scratch` names a host-side stand-in, not device memory: its device address is
+// taken once per device (with that device current) and only that address is ever passed
+// to kernels.  Calls share their GPU's copy and leave its contents to the next call, so
+// calls that overlap on one GPU race.
+// ------------------------------------------------------------------------------------
+constexpr size_t kStaticScratchBytes = DJV_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`.
+djv_status static_scratch(void** out) {
+    int dev = -1;
+    DJV_HIP(hipGetDevice(&dev));
+    DJV_REQUIRE(dev >= 0 && dev < kMaxDevices, DJV_EUNSUPPORTED, "device %d: at most %d devices", dev,
+                kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        DJV_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        DJV_REQUIRE(p != nullptr, DJV_EHIP, "hipGetSymbolAddress(scratch) gave no address");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return DJV_OK;
+}
 
 constexpr int kMaxSelect = 65536;
 constexpr int kMaxRowBytes = 256 * 8 * 16;  // one row: 256 threads x 8 vectors of 16 bytes
@@ -766,10 +799,9 @@ djv_status dejavu_predict(djv_dtype wt, int B, int d, int r, int n_out, const fl
     return run_predict(wt == DJV_F16, B, d, r, plain_input(y), &j, 1, w.mf, (hipStream_t)stream);
 }
 
-static djv_status mlp_common(djv_dtype wt, int B, int d, int N, const float* y, const void* W1,
-                             const void* b1, const void* W2, const int32_t* idx,
-                             const int32_t* count, int cap, const float* resid, float* out,
-                             void* ws, size_t ws_bytes, void* stream) {
+static djv_status check_mlp_args(djv_dtype wt, int B, int d, int N, const float* y, const void* W1,
+                                 const void* b1, const void* W2, int cap, const float* resid,
+                                 float* out) {
     DJV_TRY(check_dtype(wt));
     DJV_TRY(check_batch(B));
     DJV_TRY(check_rowlen(d, wt, "d"));
@@ -782,11 +814,24 @@ static djv_status mlp_common(djv_dtype wt, int B, int d, int N, const float* y, 
     DJV_TRY(check_ptr(W2, "W2"));
     DJV_TRY(check_opt_ptr(resid, "resid"));
     DJV_TRY(check_ptr(out, "out"));
-    const bool f16 = wt == DJV_F16;
+    return DJV_OK;
+}
+
+// Scratch bytes of an MLP call (valid arguments).
+static size_t mlp_ws_need(djv_dtype wt, int B, int d, int cap) {
     Arena sz(nullptr);
+    plan_mlp(sz, B, d, cap, wt == DJV_F16, wide_possible(wt, {d}));
+    return sz.off;
+}
+
+static djv_status mlp_common(djv_dtype wt, int B, int d, int N, const float* y, const void* W1,
+                             const void* b1, const void* W2, const int32_t* idx,
+                             const int32_t* count, int cap, const float* resid, float* out,
+                             void* ws, size_t ws_bytes, void* stream) {
+    DJV_TRY(check_mlp_args(wt, B, d, N, y, W1, b1, W2, cap, resid, out));
+    const bool f16 = wt == DJV_F16;
     const bool wide = wide_possible(wt, {d});
-    plan_mlp(sz, B, d, cap, f16, wide);
-    DJV_TRY(check_ws(ws, ws_bytes, sz.off));
+    DJV_TRY(check_ws(ws, ws_bytes, mlp_ws_need(wt, B, d, cap)));
     Arena A(ws);
     const MlpWs w = plan_mlp(A, B, d, cap, f16, wide);
     return run_mlp(f16, B, d, N, plain_input(y), W1, b1, W2, idx, count, cap, resid, out, nullptr,
@@ -800,6 +845,23 @@ djv_status dejavu_sparse_mlp(djv_dtype wt, int B, int d, int N, const float* y, 
     DJV_TRY(check_idx_ptr(idx, "idx"));
     DJV_TRY(check_idx_ptr(count, "count"));
     return mlp_common(wt, B, d, N, y, W1, b1, W2, idx, count, cap, resid, out, ws, ws_bytes, stream);
+}
+
+djv_status dejavu_sparse_mlp_no_alloc(djv_dtype wt, int B, int d, int N, const float* y,
+                                      const void* W1, const void* b1, const void* W2,
+                                      const int32_t* idx, const int32_t* count, int cap,
+                                      const float* resid, float* out, void* stream) {
+    DJV_TRY(check_idx_ptr(idx, "idx"));
+    DJV_TRY(check_idx_ptr(count, "count"));
+    DJV_TRY(check_mlp_args(wt, B, d, N, y, W1, b1, W2, cap, resid, out));
+    const size_t need = mlp_ws_need(wt, B, d, cap);
+    DJV_REQUIRE(need <= kStaticScratchBytes, DJV_EUNSUPPORTED,
+                "this call needs %zu bytes of scratch; the static scratch holds %zu (use "
+                "dejavu_sparse_mlp with a workspace)", need, kStaticScratchBytes);
+    void* ptr = nullptr;
+    DJV_TRY(static_scratch(&ptr));
+    return mlp_common(wt, B, d, N, y, W1, b1, W2, idx, count, cap, resid, out, ptr,
+                      kStaticScratchBytes, stream);
 }
 
 djv_status dejavu_dense_mlp(djv_dtype wt, int B, int d, int N, const float* y, const void* W1,

@@ -28,7 +28,8 @@ STATUS_NAMES = {0: "DJV_OK", -1: "DJV_EINVAL", -2: "DJV_EALIGN", -3: "DJV_EWORKS
 # every entry point declared in include/dejavu.h
 EXPORTS = [
     "dejavu_workspace_bytes", "dejavu_workspace_bytes_model", "dejavu_layernorm", "dejavu_select",
-    "dejavu_select_range", "dejavu_predict", "dejavu_sparse_mlp", "dejavu_dense_mlp",
+    "dejavu_select_range", "dejavu_predict", "dejavu_sparse_mlp", "dejavu_sparse_mlp_no_alloc",
+    "dejavu_dense_mlp",
     "dejavu_sparse_mha", "dejavu_dense_mha", "dejavu_neuron_norms", "dejavu_head_norms",
     "dejavu_sparse_layer", "dejavu_stack_decode", "dejavu_poll_device_error",
     "dejavu_set_mfma_min_batch", "dejavu_gather_rows", "dejavu_profile_kernel", "dejavu_profile_count",
@@ -88,6 +89,7 @@ def lib() -> ctypes.CDLL:
             "dejavu_head_norms": [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _F, _P, _P, _SZ, _P],
             "dejavu_predict": [_I, _I, _I, _I, _I, _P, _P, _P, _I, _I, _F, _P, _P, _P, _P, _SZ, _P],
             "dejavu_sparse_mlp": [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _SZ, _P],
+            "dejavu_sparse_mlp_no_alloc": [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P],
             "dejavu_dense_mlp": [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
             "dejavu_sparse_mha": [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _F,
                                   _P, _P, _P, _SZ, _P],
@@ -225,6 +227,16 @@ def dejavu_sparse_mlp(wt, B, d, N, y, W1, b1, W2, idx, count, cap, resid, out, w
     _check(lib().dejavu_sparse_mlp(wt, B, d, N, _ptr(y), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(idx),
                                    _ptr(count), cap, _ptr(resid), _ptr(out), wp, wb,
                                    _stream(stream)))
+
+
+def dejavu_sparse_mlp_no_alloc(wt, B, d, N, y, W1, b1, W2, idx, count, cap, resid, out,
+                               stream=None) -> None:
+    _check(lib().dejavu_sparse_mlp_no_alloc(wt, B, d, N, _ptr(y), _ptr(W1), _ptr(b1), _ptr(W2),
+                                            _ptr(idx), _ptr(count), cap, _ptr(resid), _ptr(out),
+                                            _stream(stream)))
+
+
+DJV_STATIC_SCRATCH_BYTES = 16 << 20
 
 
 def dejavu_dense_mlp(wt, B, d, N, y, W1, b1, W2, resid, out, ws, stream=None) -> None:

@@ -144,6 +144,27 @@ djv_status dejavu_sparse_mlp(djv_dtype wt, int B, int d, int N, const float* y,
                              void* ws, size_t ws_bytes, void* stream);
 
 /* --------------------------------------------------------------------------------------
+ * dejavu_sparse_mlp_no_alloc -- dejavu_sparse_mlp without a workspace, for callers that
+ *   cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ *   harnesses that forbid hipMalloc).  Same arguments, result and errors as
+ *   dejavu_sparse_mlp (bit-identical output), minus ws / ws_bytes: its scratch is a
+ *   static device array of DJV_STATIC_SCRATCH_BYTES that each GPU holds until the process
+ *   ends, its address taken on the first call on each device.  The call allocates nothing
+ *   (no hipMalloc, no library allocation).  A call whose scratch (dejavu_sparse_mlp's
+ *   workspace for these B, d, cap) exceeds DJV_STATIC_SCRATCH_BYTES returns
+ *   DJV_EUNSUPPORTED before any HIP call; 16 MiB holds, e.g., the OPT-175B-shaped MLP
+ *   (d 12288, N 49152) at B = 1 for any cap, and at B <= 4 with 5% of neurons per token.
+ *   Every call on a GPU shares that GPU's scratch and leaves its contents to the next
+ *   (nothing in it needs to start at zero): calls that overlap on one GPU, on different
+ *   streams or threads, race and give undefined results.
+ * ------------------------------------------------------------------------------------ */
+#define DJV_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+djv_status dejavu_sparse_mlp_no_alloc(djv_dtype wt, int B, int d, int N, const float* y,
+                                      const void* W1, const void* b1, const void* W2,
+                                      const int32_t* idx, const int32_t* count, int cap,
+                                      const float* resid, float* out, void* stream);
+
+/* --------------------------------------------------------------------------------------
  * dejavu_gather_rows -- the unfused form of the gather, for the fusion ablation:
  *   out[slot * rpu + j] = W[idx[slot] * rpu + j] for slot < count and 0 <= j < rpu, and
  *   zero rows for count <= slot < cap (rows of `cols` elements of dtype wt).

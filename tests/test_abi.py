@@ -135,6 +135,33 @@ def test_mlp_argument_errors():
         == dj.DJV_EWORKSPACE
 
 
+def test_mlp_no_alloc_argument_errors():
+    """The allocation-free MLP rejects what dejavu_sparse_mlp rejects, and calls whose scratch
+    exceeds the static buffer, all before its first HIP call."""
+    f = dj.dejavu_sparse_mlp_no_alloc
+    ok = dict(wt=dj.DJV_F32, B=1, d=768, N=3072, y=A, W1=A, b1=A, W2=A, idx=A, count=A, cap=154,
+              resid=None, out=A)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return _status(f, **a)
+    assert call(cap=0) == dj.DJV_EINVAL
+    assert call(cap=3073) == dj.DJV_EINVAL
+    assert call(idx=None) == dj.DJV_EINVAL
+    assert call(count=A + 2) == dj.DJV_EALIGN
+    assert call(W1=MIS) == dj.DJV_EALIGN
+    assert call(out=None) == dj.DJV_EINVAL
+    assert call(B=6) == dj.DJV_EUNSUPPORTED
+    # the OPT-175B MLP fits at batch 1 with every neuron; at batch 32 it does not
+    need = dj.dejavu_workspace_bytes(32, 12288, 49152, 0, 0, 0, 0)
+    assert need > dj.DJV_STATIC_SCRATCH_BYTES
+    big = dict(wt=dj.DJV_F16, d=12288, N=49152)
+    assert call(B=32, cap=49152, **big) == dj.DJV_EUNSUPPORTED
+    assert "static scratch" in dj.dejavu_last_error()
+    assert dj.dejavu_workspace_bytes(1, 12288, 49152, 0, 0, 0, 0) <= dj.DJV_STATIC_SCRATCH_BYTES
+
+
 def test_mha_argument_errors():
     f = dj.dejavu_sparse_mha
     ok = dict(wt=dj.DJV_F16, B=1, d=768, h=12, dh=64, n=128, n_cap=129, y=A, Wqkv=A, Wo=A, Kc=A,

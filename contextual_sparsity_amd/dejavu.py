@@ -13,7 +13,9 @@ import os
 from typing import Optional, Sequence
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libdejavu.so")
+# DEJAVU_LIB selects another build of the same library (e.g. the sanitizer build of the
+# host code); by default the in-tree libdejavu.so
+LIB_PATH = os.environ.get("DEJAVU_LIB") or os.path.join(PKG, "libdejavu.so")
 
 DJV_OK, DJV_EINVAL, DJV_EALIGN, DJV_EWORKSPACE, DJV_EUNSUPPORTED, DJV_EHIP = 0, -1, -2, -3, -4, -5
 DJV_F32, DJV_F16 = 0, 1

@@ -57,11 +57,20 @@ typedef enum {
     DJV_EHIP = -5          /* a HIP runtime call or kernel launch failed */
 } djv_status;
 
-typedef enum { DJV_F32 = 0, DJV_F16 = 1 } djv_dtype;
+/* The two range enumerators make every int a value of the type (also in C++), so an
+ * argument outside the listed values is well defined and returns DJV_EINVAL. */
+typedef enum {
+    DJV_F32 = 0,
+    DJV_F16 = 1,
+    DJV_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+    DJV_DTYPE_RANGE_MAX_ = 2147483647
+} djv_dtype;
 
 typedef enum {
-    DJV_TOPK = 0,      /* keep the k best-scoring units */
-    DJV_THRESHOLD = 1  /* keep the units whose sigmoid score exceeds t */
+    DJV_TOPK = 0,       /* keep the k best-scoring units */
+    DJV_THRESHOLD = 1,  /* keep the units whose sigmoid score exceeds t */
+    DJV_MODE_RANGE_MIN_ = -2147483647 - 1,
+    DJV_MODE_RANGE_MAX_ = 2147483647
 } djv_mode;
 
 /* Device flag bits reported by dejavu_poll_device_error. */

@@ -469,7 +469,7 @@ def lazy_kv(args) -> int:
         dj.dejavu_stack_decode(models[0], desc, x, True, False, None, ws, stream)  # warm-up
         for w in layers:
             w["kv_len"].fill_(n0)
-        us, recomputed = [], []
+        us, recomputed, heads_back = [], [], []
         for t in range(T):
             # a step at position n reads the lengths in half n % 2 and writes half (n + 1) % 2
             n = n0 + t
@@ -487,12 +487,26 @@ def lazy_kv(args) -> int:
                 after = torch.stack([w["kv_len"][(n + 1) % 2] for w in layers])
                 sel = after == n + 1
                 recomputed.append(int(((n - before).clamp(min=0) * sel).sum().item()))
+                heads_back.append(int((((n - before) > 0) & sel).sum().item()))
         out[f"{name}_us_per_layer"] = round(sum(us) / T, 2)
         out[f"{name}_us_per_layer_first_last"] = [round(us[0], 2), round(us[-1], 2)]
         if name == "lazy":
             out["kv_positions_recomputed_per_step"] = round(sum(recomputed) / T, 1)
             out["kv_positions_recomputed_by_step"] = recomputed
+            out["heads_caught_up_per_step"] = round(sum(heads_back) / T, 1)
+            # algorithmic bytes of the lazy launches of a step: W^K and W^V rows of every head
+            # that catches up, the saved input of every recomputed position and batch row, the
+            # recomputed cache rows, and the save of the step's own input (every layer)
+            e = 2 if s.dtype == "f16" else 4
+            step_bytes = [hb * 2 * s.dh * s.d * e + rc * s.B * (s.d * 4 + 2 * s.dh * e) + L * s.B * s.d * 4
+                          for hb, rc in zip(heads_back, recomputed)]
+            out["lazy_bytes_per_layer"] = round(sum(step_bytes) / T / L)
     out["lazy_overhead_us_per_layer"] = round(out["lazy_us_per_layer"] - out["plain_us_per_layer"], 2)
+    # the lazy launches' bytes over the time they add to the step (their own launch included)
+    out["lazy_overhead_GBps"] = round(out["lazy_bytes_per_layer"] / (out["lazy_overhead_us_per_layer"] * 1e-6)
+                                      / 1e9, 1) if out["lazy_overhead_us_per_layer"] > 0 else None
+    out["lazy_overhead_frac_of_8TBs"] = round(out["lazy_overhead_GBps"] / HBM_PEAK_GBS, 4) \
+        if out["lazy_overhead_GBps"] else None
     print(json.dumps(out), flush=True)
     return 0
 

@@ -18,8 +18,10 @@ __global__ __launch_bounds__(kThreads) void select_rows_kernel(SelectJobs jobs, 
     finish_row(S, J, blockIdx.x, B, (J.n_out + 31) / 32);
 }
 
-// Rows of at most 1024 scores: one block per selection over all B rows (small B), or one
-// block per row writing the row's bitmap for compact_kernel (larger B).
+// Rows of at most kShortRows scores: one block per selection over all B rows (small B), or
+// one block per row writing the row's bitmap for compact_kernel (larger B).  Rank counting
+// is n^2 comparisons on one compute unit (about 40 us at n = 1024), so longer rows take the
+// candidate radix path of select_rows_kernel (about 8 us at n = 1024).
 __global__ __launch_bounds__(kThreads) void select_small_kernel(SelectJobs jobs, int B) {
     __shared__ SmallShared<kThreads> S;
     select_small_block<kThreads>(S, jobs.j[blockIdx.x], B);
@@ -64,7 +66,7 @@ hipError_t launch_select(const SelectJob* jobs, int njobs, int B, hipStream_t s,
     bool small = true;
     for (int i = 0; i < njobs; ++i) {
         js.j[i] = jobs[i];
-        small = small && jobs[i].n_out <= kThreads;
+        small = small && jobs[i].n_out <= kShortRows;
     }
     if (small && B < kSmallRowsFrom) {
         prof_begin(prof, s);

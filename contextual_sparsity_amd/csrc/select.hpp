@@ -584,9 +584,36 @@ __device__ __forceinline__ void select_union_block(RowShared& S, const SelectJob
 // ---------------------------------------------------------------------------------
 template <int NT>
 struct SmallShared {
-    uint32_t keys[NT];
+    __align__(16) uint32_t keys[NT];
     int wtot[NT / kWave];
 };
+
+// Rank of `key` (thread tid's) among the n keys in LDS: keys above it plus equal keys at
+// smaller indices.  Entries n .. NT-1 hold 0, below every real key (NaN and -inf map to
+// 0x007FFFFF), so they never count.  Sixteen keys per step, four per 16-byte broadcast
+// read, so the reads of a step are in flight together.
+template <int NT>
+__device__ __forceinline__ int small_rank(const SmallShared<NT>& S, uint32_t key, int n) {
+    static_assert(NT % 16 == 0, "whole steps of sixteen keys");
+    const uint4* k4 = reinterpret_cast<const uint4*>(S.keys);
+    const int tid = threadIdx.x;
+    int rank = 0;
+    for (int j0 = 0; j0 < n; j0 += 16) {  // j0 + 16 <= NT
+        uint4 q[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) q[u] = k4[j0 / 4 + u];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t kj[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = j0 + 4 * u + e;
+                rank += (kj[e] > key || (kj[e] == key && j < tid)) ? 1 : 0;
+            }
+        }
+    }
+    return rank;
+}
 
 template <int NT>
 __device__ __forceinline__ void select_small_block(SmallShared<NT>& S, const SelectJob& J, int B) {
@@ -600,11 +627,7 @@ __device__ __forceinline__ void select_small_block(SmallShared<NT>& S, const Sel
         } else {
             S.keys[tid] = tid < n ? key : 0u;
             __syncthreads();
-            int rank = 0;
-            for (int j = 0; j < n; ++j) {
-                const uint32_t kj = S.keys[j];
-                rank += (kj > key || (kj == key && j < tid)) ? 1 : 0;
-            }
+            const int rank = small_rank<NT>(S, key, n);
             sel = sel || (tid < n && rank < J.k);
             __syncthreads();
         }
@@ -637,11 +660,7 @@ __device__ __forceinline__ void select_small_row_bits(SmallShared<NT>& S, const 
     } else {
         S.keys[tid] = tid < n ? key : 0u;
         __syncthreads();
-        int rank = 0;
-        for (int j = 0; j < n; ++j) {
-            const uint32_t kj = S.keys[j];
-            rank += (kj > key || (kj == key && j < tid)) ? 1 : 0;
-        }
+        const int rank = small_rank<NT>(S, key, n);
         sel = tid < n && rank < J.k;
     }
     const unsigned long long m = __ballot(sel);

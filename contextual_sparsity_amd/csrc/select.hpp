@@ -41,22 +41,25 @@ constexpr int kMaxBins = 4096;                     // first digit: the top 12 bi
 constexpr int kMaxCand = 4096;                     // candidates refined in LDS
 constexpr int kSample = 2048;                      // sample scores that bracket the k-th key
 
-// Exclusive prefix sum over a block of NT threads; also returns the block total.
-template <int NT>
-__device__ __forceinline__ int block_exclusive_scan(int v, int* wtot, int* total) {
+// Exclusive prefix sum over a block of NT threads; also returns the block total.  T is
+// int, or uint32_t for sums of two packed 16-bit counts (modular, no carry between them
+// while the low count's total stays below 2^16).
+template <typename T> struct NoDeduce { using type = T; };
+template <int NT, typename T = int>
+__device__ __forceinline__ T block_exclusive_scan(typename NoDeduce<T>::type v, T* wtot, T* total) {
     const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
-    int x = v;
+    T x = v;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
-        const int y = __shfl_up(x, o, kWave);
+        const T y = __shfl_up(x, o, kWave);
         if (lane >= o) x += y;
     }
     if (lane == kWave - 1) wtot[w] = x;
     __syncthreads();
-    int base = 0, tot = 0;
+    T base = 0, tot = 0;
 #pragma unroll
     for (int q = 0; q < NT / kWave; ++q) {
-        const int t = wtot[q];
+        const T t = wtot[q];
         if (q < w) base += t;
         tot += t;
     }
@@ -66,41 +69,70 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wtot, int* total
 }
 
 // The digit of the rem-th largest key among histogrammed keys.  Thread t owns the PER
-// bins nbins-1-PER*t .. nbins-PER*t, so thread order is descending digit order.  rem
-// (in: rank among the keys, out: rank inside the returned bin) is updated in every thread.
-template <int NT, int PER>
-__device__ __forceinline__ int find_bin_counts(const int (&c)[PER], int nbins, int& rem, int* wtot,
-                                               int* sh) {
+// bins nbins-1-PER*t .. nbins-PER*t, so thread order is descending digit order.  rem (in:
+// rank among the keys, from 1; out: rank inside the returned bin) is updated in every
+// thread.  The threads' bin sums go to LDS and one wave finds the bin: each lane sums 16
+// threads' sums, a wave scan finds the lane where the rank falls, that lane walks its
+// threads and then the found thread's bins.  Two block barriers in all (a block-wide scan
+// takes four and a longer chain of LDS round trips).
+template <int PER>
+__device__ __forceinline__ int find_bin(const uint32_t* hist, int nbins, int& rem, int* part, int* sh) {
+    constexpr int kPerLane = kThreads / kWave;  // thread sums per lane
     const int tid = threadIdx.x;
     int s = 0;
 #pragma unroll
-    for (int q = 0; q < PER; ++q) s += c[q];
-    int total;
-    int cum = block_exclusive_scan<NT>(s, wtot, &total);
-#pragma unroll
     for (int q = 0; q < PER; ++q) {
-        if (cum < rem && rem <= cum + c[q]) {
-            sh[0] = nbins - 1 - PER * tid - q;
-            sh[1] = rem - cum;
+        const int bin = nbins - 1 - PER * tid - q;
+        s += bin >= 0 ? (int)hist[bin] : 0;
+    }
+    part[tid] = s;
+    __syncthreads();
+    if (tid < kWave) {
+        const int l = tid;
+        int v[kPerLane];
+        const int4* p4 = reinterpret_cast<const int4*>(part + l * kPerLane);
+#pragma unroll
+        for (int i = 0; i < kPerLane / 4; ++i) {
+            const int4 t = p4[i];
+            v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
         }
-        cum += c[q];
+        int tot = 0;
+#pragma unroll
+        for (int i = 0; i < kPerLane; ++i) tot += v[i];
+        int inc = tot;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int y = __shfl_up(inc, o, kWave);
+            if (l >= o) inc += y;
+        }
+        const int exc = inc - tot;
+        if (exc < rem && rem <= inc) {  // one lane (when rem is within the total)
+            int cum = exc, t = -1, cum_t = 0;
+#pragma unroll
+            for (int i = 0; i < kPerLane; ++i) {
+                if (t < 0 && rem <= cum + v[i]) {
+                    t = l * kPerLane + i;
+                    cum_t = cum;
+                }
+                cum += v[i];
+            }
+#pragma unroll
+            for (int q = 0; q < PER; ++q) {
+                const int bin = nbins - 1 - PER * t - q;
+                const int c = bin >= 0 ? (int)hist[bin] : 0;
+                if (cum_t < rem && rem <= cum_t + c) {
+                    sh[0] = bin;
+                    sh[1] = rem - cum_t;
+                }
+                cum_t += c;
+            }
+        }
     }
     __syncthreads();
     const int d = sh[0];
     rem = sh[1];
-    __syncthreads();
+    __syncthreads();  // every thread has read sh (and part) before either is written again
     return d;
-}
-
-template <int NT, int PER>
-__device__ __forceinline__ int find_bin(const uint32_t* hist, int nbins, int& rem, int* wtot, int* sh) {
-    int c[PER];
-#pragma unroll
-    for (int q = 0; q < PER; ++q) {
-        const int bin = nbins - 1 - PER * (int)threadIdx.x - q;
-        c[q] = bin >= 0 ? (int)hist[bin] : 0;
-    }
-    return find_bin_counts<NT, PER>(c, nbins, rem, wtot, sh);
 }
 
 // Lanes of a wave hold 64 consecutive indices starting at index j0 (a multiple of 64):
@@ -152,6 +184,7 @@ struct RowShared {
     int cand_j[kMaxCand];
     int sh[4];
     int wtot[kThreads / kWave];
+    __align__(16) int part[kThreads];     // per-thread bin sums of find_bin
 };
 
 // Radix select over candidate keys in LDS, from digit `first` (0: the top 12 bits, 1 and
@@ -170,8 +203,8 @@ __device__ __forceinline__ void resolve_candidates(RowShared& S, int ncand, uint
         for (int i = tid; i < ncand; i += kThreads)
             if ((S.cand[i] & pmask) == prefix) atomicAdd(&S.hist[(S.cand[i] >> shift) & dmask], 1u);
         __syncthreads();
-        const uint32_t d = pass == 0 ? (uint32_t)find_bin<kThreads, 4>(S.hist, kMaxBins, rem, S.wtot, S.sh)
-                                     : (uint32_t)find_bin<kThreads, 1>(S.hist, 1024, rem, S.wtot, S.sh);
+        const uint32_t d = pass == 0 ? (uint32_t)find_bin<4>(S.hist, kMaxBins, rem, S.part, S.sh)
+                                     : (uint32_t)find_bin<1>(S.hist, 1024, rem, S.part, S.sh);
         prefix |= d << shift;
         pmask |= dmask << shift;
     }
@@ -286,7 +319,7 @@ __device__ __forceinline__ void select_row_radix(RowShared& S, const SelectJob& 
         }
         __syncthreads();
         int rem = J.k;
-        const uint32_t top = (uint32_t)find_bin<kThreads, 4>(S.hist, kMaxBins, rem, S.wtot, S.sh);
+        const uint32_t top = (uint32_t)find_bin<4>(S.hist, kMaxBins, rem, S.part, S.sh);
         uint32_t prefix = top << 20, pmask = 0xFFF00000u;
         const int ncand = (int)S.hist[top];
         __syncthreads();  // every thread has read ncand before either branch rewrites hist
@@ -342,7 +375,7 @@ __device__ __forceinline__ void select_row_radix(RowShared& S, const SelectJob& 
                     }
                 }
                 __syncthreads();
-                prefix |= (uint32_t)find_bin<kThreads, 4>(S.hist, 1024, rem, S.wtot, S.sh) << shift;
+                prefix |= (uint32_t)find_bin<4>(S.hist, 1024, rem, S.part, S.sh) << shift;
                 pmask |= 1023u << shift;
             }
     #pragma unroll 1
@@ -459,11 +492,11 @@ __device__ __forceinline__ bool select_row_fast(RowShared& S, const SelectJob& J
     uint32_t b_hi = kMaxBins - 1, b_lo = 0x7;  // 0x7: the lowest digit of a real key (NaN, -inf)
     if (rho - margin >= 1) {
         int r = rho - margin;
-        b_hi = (uint32_t)find_bin<kThreads, 4>(S.hist, kMaxBins, r, S.wtot, S.sh);
+        b_hi = (uint32_t)find_bin<4>(S.hist, kMaxBins, r, S.part, S.sh);
     }
     if (rho + margin <= kSample) {
         int r = rho + margin;
-        b_lo = (uint32_t)find_bin<kThreads, 4>(S.hist, kMaxBins, r, S.wtot, S.sh);
+        b_lo = (uint32_t)find_bin<4>(S.hist, kMaxBins, r, S.part, S.sh);
     }
     // as 16-bit bounds: above means hk > hi16, inside means lo16 <= hk <= hi16
     const uint32_t hi16 = (b_hi << 4) | 15u, lo16 = b_lo << 4;
@@ -481,9 +514,13 @@ __device__ __forceinline__ bool select_row_fast(RowShared& S, const SelectJob& J
         S.sh[2] = (int)hi16;
         S.sh[3] = (int)lo16;
     }
-    int above, inside;
-    (void)block_exclusive_scan<kThreads>(ca, S.wtot, &above);
-    int at = block_exclusive_scan<kThreads>(cm, S.wtot, &inside);
+    // both counts in one scan: above in the low 16 bits, inside in the high 16 (each at most
+    // the row's 49152 keys, so neither part carries into the other)
+    uint32_t tot2;
+    const uint32_t at2 = block_exclusive_scan<kThreads, uint32_t>((uint32_t)ca | ((uint32_t)cm << 16),
+                                                                 reinterpret_cast<uint32_t*>(S.wtot), &tot2);
+    const int above = (int)(tot2 & 0xFFFFu), inside = (int)(tot2 >> 16);
+    int at = (int)(at2 >> 16);
     if (!(above < k && k <= above + inside && inside <= kMaxCand)) return false;  // uniform
 
     // keys above the bracket are kept; the indices inside are gathered.  The bounds are

@@ -20,9 +20,12 @@
 // bits) finds the k-th key; keys equal to it are taken in index order.  The bracket only
 // decides how much work is done, never the result: when the check fails (a sample far
 // off, or heavy ties), and for rows above 49152, the row falls back to a radix select
-// over all keys, reloading them per pass.  Threshold rows are ballots of key > tau.  With one row the block compacts
-// the result into the ascending index list and the device-side count; several rows are
-// ORed (in LDS for a side block, or by a second kernel).  A tensor-parallel shard lists
+// over all keys, reloading them per pass.  Threshold rows are ballots of key > tau.
+// Every search for the bin holding a rank is done by one wave over the threads' bin sums
+// (find_bin).  With one row the block compacts the result into the ascending index list
+// and the device-side count; several rows are ORed (in LDS for a side block, or by a
+// second kernel).  Rows of at most 256 scores (the head predictor) take a smaller path:
+// one key per thread, ranks by counting (select_small_block).  A tensor-parallel shard lists
 // only the kept units of its own range [lo, hi), rebased to its rows (j - lo): the
 // selection itself is over all units, as every shard computes it alike.
 //

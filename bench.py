@@ -78,6 +78,8 @@ def parse(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget")
     ap.add_argument("--breakdown", action="store_true", help="time every kernel family")
     ap.add_argument("--no-lookahead", action="store_true", help="serial schedule for any workload")
+    ap.add_argument("--deterministic", action="store_true",
+                    help="bitwise-reproducible lookahead stack (fixed-order reductions, finalize launches)")
     ap.add_argument("--lookahead", action="store_true",
                     help="lookahead schedule for any workload (the single-layer workloads default to "
                          "the serial one: head set from LN(x), neuron set from LN(x'))")
@@ -582,6 +584,10 @@ def main(argv=None) -> int:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no "
               "multi-GPU path", file=sys.stderr)
         return 2
+    if args.deterministic:
+        import torch  # noqa: F401  (torch's HIP runtime is loaded before the library's)
+        from contextual_sparsity_amd import dejavu as dj
+        dj.dejavu_set_deterministic(True)
     if args.sweep:
         return sweep(args)
     if args.lazy_kv:
@@ -859,7 +865,7 @@ def main(argv=None) -> int:
         "config": {"workload": wl.name, "layers": L, "d": s.d, "N": s.N, "h": s.h, "dh": s.dh,
                    "n": s.n, "r": s.r, "batch": s.B, "keep_neurons_pct": wl.pct_M,
                    "keep_heads_pct": wl.pct_A, "k_M": k_M, "k_A": k_A, "lookahead": lookahead,
-                   "union_sets": unions},
+                   "deterministic": args.deterministic, "union_sets": unions},
         "us_per_layer": round(ms_step * 1e3 / L, 2),
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "copy_ref_GBps": round(copy_gbs, 1),

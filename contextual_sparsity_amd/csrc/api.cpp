@@ -95,7 +95,7 @@ djv_status static_scratch(void** out) {
 }
 
 constexpr int kMaxSelect = 65536;
-constexpr int kMaxRowBytes = 256 * 8 * 16;  // one row: 256 threads x 8 vectors of 16 bytes
+constexpr int kMaxRowBytes = kMaxRowVecs * 16;  // one row: 256 threads x 8 vectors of 16 bytes
 
 size_t esize(int wt) { return wt == DJV_F16 ? 2 : 4; }
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -179,6 +179,8 @@ uint32_t tau_key(float t) {
 // Batches of at least this many rows use the matrix-core kernels where they can (fp16
 // weights, row lengths divisible by 32); batches above kMaxBatch always do.
 std::atomic<int> g_mfma_min_batch{kMaxBatch + 1};
+// When set, the lookahead stack keeps its finalize launches (bitwise reproducible).
+std::atomic<int> g_deterministic{0};
 
 bool wide_possible(int wt, std::initializer_list<int> cols) {
     if (wt != DJV_F16) return false;
@@ -352,6 +354,14 @@ RowInput ln_input(const float* x, const float2* stats, const LayerWs& w, float e
     in.eps = eps;
     return in;
 }
+// LN(x) with the moments computed by the consuming GEMV (x accumulated in place).
+RowInput own_ln_input(const float* x, float eps) {
+    RowInput in{};
+    in.x = x;
+    in.eps = eps;
+    in.own_stats = true;
+    return in;
+}
 
 // ------------------------------------------------------------------------------------
 // Kernel sequences shared by the entry points (arguments already validated)
@@ -422,11 +432,13 @@ djv_status run_predict(bool f16, int B, int d, int r, const RowInput& in, const 
 // Row-axpy over the kept W2 rows: out = resid + W2_S^T a.  stats (optional) receives the
 // tile statistics of out.
 djv_status run_down(bool f16, int B, int d, const void* W2, const UnitList& neurons,
-                    const float* resid, float* out, float2* stats, const MlpWs& w, hipStream_t s) {
+                    const float* resid, float* out, float2* stats, const MlpWs& w, hipStream_t s,
+                    bool accumulate = false) {
     AxpyArgs x{};
     x.W = W2; x.cols = d; x.list = neurons; x.rpu = 1; x.coef = w.a; x.ldc = neurons.cap; x.B = B;
     x.partial = w.partial; x.rows_per_chunk = w.rpc; x.resid = resid;
     x.out = out; x.stats = stats; x.mfma = w.mf.on; x.flags = device_flags(); x.prof = DJV_PROF_MLP_DOWN;
+    x.accumulate = accumulate;
     DJV_HIP(launch_axpy(f16, x, s));
     return DJV_OK;
 }
@@ -466,11 +478,13 @@ djv_status run_attend(bool f16, int B, int h, int dh, int n, int n_cap, void* Kc
 // Row-axpy over the kept heads' W_O rows: out = resid + sum_i H_i W_i^O (H merged from
 // the attention chunks here when fused).
 djv_status run_oproj(bool f16, int B, int d, int dh, int n, const void* Wo, const UnitList& heads,
-                     const float* resid, float* out, float2* stats, const MhaWs& w, hipStream_t s) {
+                     const float* resid, float* out, float2* stats, const MhaWs& w, hipStream_t s,
+                     bool accumulate = false) {
     AxpyArgs x{};
     x.W = Wo; x.cols = d; x.list = heads; x.rpu = dh; x.coef = w.H; x.ldc = heads.cap * dh; x.B = B;
     x.partial = w.partial; x.rows_per_chunk = w.rpc; x.resid = resid; x.out = out; x.stats = stats;
     x.mfma = w.mf.on; x.flags = device_flags(); x.prof = DJV_PROF_O_PROJ;
+    x.accumulate = accumulate;
     if (w.fused) {
         x.attn_part = w.part;
         x.attn_nchunk = (n + 1 + w.chunk - 1) / w.chunk;
@@ -1018,7 +1032,16 @@ djv_status dejavu_stack_decode(const djv_model* m, const djv_layer* layers, int 
     const bool f16 = m->wt == DJV_F16;
     Arena A(ws);
     const LayerWs w = plan_layer(A, *m, dense != 0);
-    DJV_HIP(launch_ln_stats(m->B, m->d, x, w.s_in, sm));
+    // Unless the caller asks for bitwise-reproducible results, the lookahead stack in the
+    // vector-ALU form keeps the residual stream in x itself: the O-projection and MLP-down
+    // row-axpys add their products to it with fp32 atomics and the GEMVs that read LN(x)
+    // sum its moments themselves, so no finalize launch follows either projection.  Lazy
+    // K/V (which reads tile statistics) and the matrix-core form use the finalize.
+    bool lazy = false;
+    for (int l = 0; l < L; ++l) lazy = lazy || layers[l].Y != nullptr;
+    const bool in_place = lookahead && !dense && !w.mf.on && !lazy &&
+                          !g_deterministic.load(std::memory_order_relaxed);
+    if (!in_place) DJV_HIP(launch_ln_stats(m->B, m->d, x, w.s_in, sm));
 
     if (dense) {
         for (int l = 0; l < L; ++l) {
@@ -1054,7 +1077,7 @@ djv_status dejavu_stack_decode(const djv_model* m, const djv_layer* layers, int 
     {
         // layer 0's scores from LN(x_0); S_A^0 alone, S_M^0 in layer 0's Q/K/V launch
         const LayerIO io0 = layer_io(x, w, 0, L);
-        const RowInput in0 = ln_input(io0.x_in, io0.s_in, w, m->eps);
+        const RowInput in0 = in_place ? own_ln_input(x, m->eps) : ln_input(io0.x_in, io0.s_in, w, m->eps);
         const PredJob ja = job_A(*m, layers[0], w, 0, trace, 0), jm = job_M(*m, layers[0], w, 0, trace, 0);
         GemvArgs g = gemv_args(m->d, m->B, DJV_PROF_PRED_1, w.mf);
         add_seg(g, seg_first(ja, m->r, in0));
@@ -1071,8 +1094,8 @@ djv_status dejavu_stack_decode(const djv_model* m, const djv_layer* layers, int 
         const int cur = l & 1, nxt = (l + 1) & 1;
         const bool ahead = l + 1 < L;
         const djv_layer& Ly = layers[l];
-        const LayerIO io = layer_io(x, w, l, L);
-        const RowInput in_a = ln_input(io.x_in, io.s_in, w, m->eps);
+        const LayerIO io = in_place ? LayerIO{x, nullptr, x, nullptr} : layer_io(x, w, l, L);
+        const RowInput in_a = in_place ? own_ln_input(x, m->eps) : ln_input(io.x_in, io.s_in, w, m->eps);
         const UnitList heads{w.idxA[cur], count_of(*m, w.cntA[cur]), capA, m->h};
         const UnitList neurons{w.idxM[cur], count_of(*m, w.cntM[cur]), capM, m->N};
         PredJob na{}, nm{};
@@ -1113,16 +1136,26 @@ djv_status dejavu_stack_decode(const djv_model* m, const djv_layer* layers, int 
                 DJV_HIP(launch_gemv(f16, g, sm));
             }
         }
-        DJV_TRY(run_oproj(f16, m->B, m->d, m->dh, m->n, Ly.Wo, heads, io.x_in, w.xm, w.sm, w.mha, sm));
+        // x' = x + attention: added to x itself (in place), else written to xm with its
+        // tile statistics
+        float* xm = in_place ? x : w.xm;
+        if (in_place)
+            DJV_TRY(run_oproj(f16, m->B, m->d, m->dh, m->n, Ly.Wo, heads, nullptr, x, nullptr, w.mha, sm, true));
+        else
+            DJV_TRY(run_oproj(f16, m->B, m->d, m->dh, m->n, Ly.Wo, heads, io.x_in, w.xm, w.sm, w.mha, sm));
         if (trace && trace->x_mid)
-            DJV_TRY(copy_async(trace->x_mid + (size_t)l * m->B * m->d, w.xm, (size_t)m->B * m->d * 4, sm));
+            DJV_TRY(copy_async(trace->x_mid + (size_t)l * m->B * m->d, xm, (size_t)m->B * m->d * 4, sm));
 
         // MLP up-projection of the kept neurons, S_A^{l+1}
         g = gemv_args(m->d, m->B, DJV_PROF_MLP_UP, w.mf);
-        add_seg(g, seg_up(Ly.W1, Ly.b1, neurons, ln_input(w.xm, w.sm, w, m->eps), w.mlp.a));
+        add_seg(g, seg_up(Ly.W1, Ly.b1, neurons,
+                          in_place ? own_ln_input(x, m->eps) : ln_input(w.xm, w.sm, w, m->eps), w.mlp.a));
         if (ahead) add_side(g, select_job(na));
         DJV_HIP(launch_gemv(f16, g, sm));
-        DJV_TRY(run_down(f16, m->B, m->d, Ly.W2, neurons, w.xm, io.x_out, io.s_out, w.mlp, sm));
+        if (in_place)
+            DJV_TRY(run_down(f16, m->B, m->d, Ly.W2, neurons, nullptr, x, nullptr, w.mlp, sm, true));
+        else
+            DJV_TRY(run_down(f16, m->B, m->d, Ly.W2, neurons, w.xm, io.x_out, io.s_out, w.mlp, sm));
     }
     return DJV_OK;
 }
@@ -1130,6 +1163,13 @@ djv_status dejavu_stack_decode(const djv_model* m, const djv_layer* layers, int 
 djv_status dejavu_set_mfma_min_batch(int b, int* previous) {
     DJV_REQUIRE(b >= 1 && b <= kMaxBatch + 1, DJV_EINVAL, "b = %d outside [1, %d]", b, kMaxBatch + 1);
     const int old = g_mfma_min_batch.exchange(b);
+    if (previous) *previous = old;
+    return DJV_OK;
+}
+
+djv_status dejavu_set_deterministic(int on, int* previous) {
+    DJV_REQUIRE(on == 0 || on == 1, DJV_EINVAL, "on = %d is not 0 or 1", on);
+    const int old = g_deterministic.exchange(on);
     if (previous) *previous = old;
     return DJV_OK;
 }

@@ -18,6 +18,10 @@
 // chunks in flight together.  It also writes (mean, M2) of every 64-column slice of out, from
 // which the next GEMV applies LayerNorm while loading.  The kernel boundary between the
 // two is what makes the partial tiles of all XCDs visible; no device-wide fence is used.
+// Accumulating form (the lookahead stack's residual stream): each block adds its tile to
+// out with fp32 atomics instead, so no partial tiles and no finalize launch; the order of
+// the additions, and with it the last bits of out, depends on scheduling, and the consumer
+// computes the LayerNorm moments itself.
 #include "common.hpp"
 
 namespace djv {
@@ -106,14 +110,15 @@ __device__ __forceinline__ void stage_attention(const AxpyArgs& a, int r0, int n
     }
 }
 
-template <typename T, int NB>
+template <typename T, int NB, bool ACC>
 __global__ __launch_bounds__(kThreads) void axpy_partial_kernel(AxpyArgs a) {
     constexpr int E = WTraits<T>::kPerVec;
     constexpr int TC = kWave * E;                       // columns per tile
     // dynamic LDS: [NB][rpc] coefficients, [rpc] rows, then (merged attention) the
     // [NB][2][nchunk] chunk maxima / weights and sums, and [NB][2] denominators
     extern __shared__ float dyn[];
-    __shared__ float red[kWavesPerBlock - 1][NB][TC];
+    // the waves' tile sums: waves 1..3 (wave 0 adds them to its own), or (ACC) all four
+    __shared__ float red[ACC ? kWavesPerBlock : kWavesPerBlock - 1][NB][TC];
 
     const int tid = threadIdx.x, wv = tid / kWave, ln = tid % kWave;
     const int chunk = blockIdx.y;
@@ -205,6 +210,33 @@ __global__ __launch_bounds__(kThreads) void axpy_partial_kernel(AxpyArgs a) {
         consume(w, i0);
     }
 
+    if constexpr (ACC) {
+        // out += the tile: the four waves' sums through LDS, then each thread adds columns
+        // tid, tid + 256, ... (one atomic instruction per 64 consecutive columns)
+        if (col_ok) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int e = 0; e < E; ++e) red[wv][b][ln * E + e] = acc[b][e];
+        }
+        __syncthreads();
+        const int c0 = blockIdx.x * TC;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            if (b >= a.B) break;
+            float* dst = a.out + (size_t)b * a.cols + c0;
+#pragma unroll
+            for (int c = tid; c < TC; c += kThreads) {
+                if (c0 + c < a.cols) {
+                    float t = red[0][b][c];
+#pragma unroll
+                    for (int q = 1; q < kWavesPerBlock; ++q) t += red[q][b][c];
+                    unsafeAtomicAdd(dst + c, t);
+                }
+            }
+        }
+        return;
+    }
     if (wv > 0) {
 #pragma unroll
         for (int b = 0; b < NB; ++b)
@@ -457,8 +489,12 @@ hipError_t dispatch_mfma(const AxpyArgs& args, hipStream_t s) {
 template <typename T>
 hipError_t dispatch(const AxpyArgs& args, hipStream_t s) {
     if (args.mfma) {
-        if constexpr (sizeof(T) == 2) return dispatch_mfma<T>(args, s);
-        else return hipErrorInvalidValue;
+        if constexpr (sizeof(T) == 2) {
+            if (args.accumulate) return hipErrorInvalidValue;
+            return dispatch_mfma<T>(args, s);
+        } else {
+            return hipErrorInvalidValue;
+        }
     }
     AxpyArgs a = args;
     a.chunk_step = kWavesPerBlock * kUnroll;
@@ -477,13 +513,20 @@ hipError_t dispatch(const AxpyArgs& args, hipStream_t s) {
         }
         dim3 grid(tiles, nch);
         prof_begin(a.prof, s);
-        if (nb == 1) hipLaunchKernelGGL((axpy_partial_kernel<T, 1>), grid, dim3(kThreads), dyn, s, a);
-        else if (nb == 2) hipLaunchKernelGGL((axpy_partial_kernel<T, 2>), grid, dim3(kThreads), dyn, s, a);
-        else hipLaunchKernelGGL((axpy_partial_kernel<T, 4>), grid, dim3(kThreads), dyn, s, a);
+        if (a.accumulate) {
+            if (nb == 1) hipLaunchKernelGGL((axpy_partial_kernel<T, 1, true>), grid, dim3(kThreads), dyn, s, a);
+            else if (nb == 2) hipLaunchKernelGGL((axpy_partial_kernel<T, 2, true>), grid, dim3(kThreads), dyn, s, a);
+            else hipLaunchKernelGGL((axpy_partial_kernel<T, 4, true>), grid, dim3(kThreads), dyn, s, a);
+        } else {
+            if (nb == 1) hipLaunchKernelGGL((axpy_partial_kernel<T, 1, false>), grid, dim3(kThreads), dyn, s, a);
+            else if (nb == 2) hipLaunchKernelGGL((axpy_partial_kernel<T, 2, false>), grid, dim3(kThreads), dyn, s, a);
+            else hipLaunchKernelGGL((axpy_partial_kernel<T, 4, false>), grid, dim3(kThreads), dyn, s, a);
+        }
         prof_end(a.prof, s);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    if (a.accumulate) return hipSuccess;
     dim3 fgrid((a.cols + kLnTile - 1) / kLnTile, a.B);
     hipLaunchKernelGGL(axpy_finalize_kernel, fgrid, dim3(kFinGroups * kFinQuads), 0, s, a);
     return hipGetLastError();

@@ -127,6 +127,7 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 
 // LayerNorm statistics travel as (mean, M2) of each kLnTile-column slice of a row.
 constexpr int kLnTile = 64;
+constexpr int kMaxRowVecs = 256 * 8;  // 16-byte vectors of the longest weight row (32 KiB)
 
 // Order-preserving key of an fp32 score: larger score, larger key; -0 = +0; NaN ranks as
 // -inf.
@@ -217,15 +218,23 @@ enum GemvEpi : int {
     kEpiQkv = 3,        // q -> out, k/v -> cache position n (rounded to the cache dtype)
 };
 
-// Activation rows fed to a GEMV: either ready rows y, or LayerNorm(x) applied on the fly
-// from per-tile statistics of x (see LnTiles).
+// Activation rows fed to a GEMV: either ready rows y, or LayerNorm(x) applied on the fly,
+// with the moments of x either combined from per-tile statistics written by the kernel
+// that produced x (see LnTiles), or (own_stats: x accumulated in place by the row-axpys,
+// which write no statistics) summed by the consumer itself from the values it loads.
 struct RowInput {
     const float* y;       // [B, cols] ready input; when nullptr, LN(x) is used
     const float* x;       // [B, cols] residual stream
     const float2* stats;  // [B, ntiles] (mean, M2) of each kLnTile-column slice of x
     int ntiles;
     float eps;
+    bool own_stats;       // moments of x from x itself (stats unused)
 };
+
+__host__ __device__ inline bool same_row_input(const RowInput& p, const RowInput& q) {
+    return p.y == q.y && p.x == q.x && p.stats == q.stats && p.ntiles == q.ntiles && p.eps == q.eps &&
+           p.own_stats == q.own_stats;
+}
 
 constexpr int kAttnMaxChunks = 1024;   // chunks per head the merge kernel accepts
 constexpr int kFuseMaxChunks = 128;    // chunks per head the O-projection merges itself
@@ -324,6 +333,11 @@ struct AxpyArgs {
     const float* resid;   // may be nullptr
     float* out;           // [B, cols]
     float2* stats;        // [B, ceil(cols / kLnTile)] (mean, M2) of each slice of out, or nullptr
+    // when set, out += the product: each block adds its tile with fp32 atomics (vector-ALU
+    // form only): no partial tiles, no finalize launch, no statistics; resid, partial and
+    // stats are unused, and the order of the additions (so the last bits of out) depends
+    // on scheduling
+    bool accumulate;
     // when set, the coefficients are the attention outputs merged here from the
     // split-position partials [B, cap, nchunk, rpu + 2] (rows of a unit = its rpu dims;
     // needs rows_per_chunk <= rpu and nchunk <= kFuseMaxChunks); coef is then unused

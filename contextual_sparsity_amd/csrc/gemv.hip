@@ -38,8 +38,7 @@ hipError_t launch_gemv(bool f16, const GemvArgs& a, hipStream_t s) {
         bool counted = false, same = true;
         for (int i = 0; i < a.nseg; ++i) {
             counted = counted || a.seg[i].list.count != nullptr;
-            const RowInput &p = a.seg[i].in, &q = a.seg[0].in;
-            same = same && p.y == q.y && p.x == q.x && p.stats == q.stats && p.ntiles == q.ntiles && p.eps == q.eps;
+            same = same && same_row_input(a.seg[i].in, a.seg[0].in);
         }
         d.dyn = counted && same;
     }

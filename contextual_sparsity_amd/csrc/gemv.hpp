@@ -23,7 +23,9 @@
 //   * Team reduction: wave butterfly, then (TS = 256) a 4-entry LDS combine.
 //   * The activation rows are either given, or LayerNorm(x) is applied while the slice is
 //     loaded, from per-slice (mean, M2) statistics written by the kernel that produced x,
-//     so no separate normalisation pass runs.
+//     so no separate normalisation pass runs.  When x was accumulated in place by atomics
+//     (no statistics), the team sums x's moments itself, one barrier; in 1024-thread
+//     blocks the whole block loads and normalises the row once, into LDS, for its teams.
 //   * One launch may serve up to three weight matrices of the same row length and input
 //     (e.g. the kept heads' Q/K/V rows and both predictors' first layers, which all read
 //     LN(x)), each with its own epilogue; the grid is shared in proportion to their rows.
@@ -228,6 +230,12 @@ __global__ __launch_bounds__(BlockOf<MODE>::value) void gemv_kernel(GemvArgs a) 
     constexpr int NT = kThreads / TS;
     constexpr int NW = TS / kWave;  // waves per team
     __shared__ float red[2][NT][NW][G * NB];
+    __shared__ float mom[2][NT][NW][NB];  // wave sums of the row moments (own_stats)
+    // several teams of several waves (1024-thread blocks): with own_stats the block loads
+    // and normalises the row once, into LDS, where every team reads its slice
+    constexpr bool kCoop = NT > 1 && NW > 1;
+    __shared__ YSlice<T> ylds[kCoop ? kMaxRowVecs : 1];
+    __shared__ float momc[2][kCoop ? kThreads / kWave : 1];
 
     const int tid = threadIdx.x;
     // a team is whole waves, so its index, and with it every row, unit and row address,
@@ -332,7 +340,8 @@ __global__ __launch_bounds__(BlockOf<MODE>::value) void gemv_kernel(GemvArgs a) 
 
     // this thread's slice of every batch row (loads clamped in range, then masked)
     YSlice<T> ys[NB][NV];
-    {
+    const bool own = !S.in.y && S.in.own_stats;  // uniform over the block
+    if (!own) {
         float raw[NB][NV][8];
 #pragma unroll
         for (int b = 0; b < NB; ++b)
@@ -353,8 +362,135 @@ __global__ __launch_bounds__(BlockOf<MODE>::value) void gemv_kernel(GemvArgs a) 
                 ys[b][i].set(raw[b][i], 0);
             }
         }
+        load_group(qb, base0 + stride + tm);
+    } else if constexpr (kCoop) {
+        // own_stats, several teams of several waves: the block's threads share the row's
+        // vectors (at most KV each), sum the row's moments over all of the block's waves
+        // (as the per-team form below), and leave the normalised row in LDS, where every
+        // team reads its slices.  The second group's weights are requested before the
+        // barrier, so they are in flight while the moments are formed.
+        static_assert(!kCoop || NB == 1, "the block-wide prologue serves one batch row");
+        constexpr int KV = (NV * TS + kThreads - 1) / kThreads;
+        float raw[KV][8];
+#pragma unroll
+        for (int k = 0; k < KV; ++k)
+            load_raw<T>(S.in, a.cols, 0, min(tid + kThreads * k, nvec - 1) * E, raw[k]);
+        load_group(qb, base0 + stride + tm);
+        const float sh = S.in.x[0];
+        float t1 = 0.f, t2 = 0.f;
+#pragma unroll
+        for (int k = 0; k < KV; ++k)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float dv = tid + kThreads * k < nvec ? raw[k][e] - sh : 0.f;
+                t1 += dv;
+                t2 = fmaf(dv, dv, t2);
+            }
+        t1 = wave_sum(t1);
+        t2 = wave_sum(t2);
+        const int wb = tid / kWave;
+        if (ln == 0) {
+            momc[0][wb] = t1;
+            momc[1][wb] = t2;
+        }
+        __syncthreads();
+        t1 = 0.f;
+        t2 = 0.f;
+#pragma unroll
+        for (int w = 0; w < kThreads / kWave; ++w) {
+            t1 += momc[0][w];
+            t2 += momc[1][w];
+        }
+        const float inv_n = 1.0f / (float)a.cols;
+        const float md = t1 * inv_n;
+        const float mean = sh + md;
+        const float rstd = 1.0f / sqrtf(fmaxf(t2 * inv_n - md * md, 0.f) + S.in.eps);
+#pragma unroll
+        for (int k = 0; k < KV; ++k) {
+            const int v = tid + kThreads * k;
+            if (v < nvec) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) raw[k][e] = (raw[k][e] - mean) * rstd;
+                YSlice<T> t;
+                t.set(raw[k], 0);
+                ylds[v] = t;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int v = lt + TS * i;
+            if (v < nvec) ys[0][i] = ylds[v];
+            else ys[0][i].zero();
+        }
+    } else {
+        // own_stats, per team (the team holds the whole row): the moments in one pass over
+        // the deviations d = x - x[0] from the row's first element, mean = x[0] + sum(d)/n
+        // and variance = (sum(d^2) - sum(d)^2/n)/n (the shift keeps the squares on the
+        // scale of the spread rather than of the mean); wave sums, then (several waves per
+        // team) a sum over the team's waves through LDS, one barrier.  The second group's
+        // weights are requested before it.
+        float raw[NB][NV][8];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const int v = min(lt + TS * i, nvec - 1);
+                load_raw<T>(S.in, a.cols, min(b, a.B - 1), v * E, raw[b][i]);
+            }
+        load_group(qb, base0 + stride + tm);
+        float sd[NB], sq[NB], sh[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            sh[b] = S.in.x[(size_t)min(b, a.B - 1) * a.cols];
+            float t1 = 0.f, t2 = 0.f;
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float dv = lt + TS * i < nvec ? raw[b][i][e] - sh[b] : 0.f;
+                    t1 += dv;
+                    t2 = fmaf(dv, dv, t2);
+                }
+            sd[b] = wave_sum(t1);
+            sq[b] = wave_sum(t2);
+        }
+        if constexpr (NW > 1) {
+            if (ln == 0) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    mom[0][tm][wv][b] = sd[b];
+                    mom[1][tm][wv][b] = sq[b];
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                float t1 = 0.f, t2 = 0.f;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) {
+                    t1 += mom[0][tm][w][b];
+                    t2 += mom[1][tm][w][b];
+                }
+                sd[b] = t1;
+                sq[b] = t2;
+            }
+        }
+        const float inv_n = 1.0f / (float)a.cols;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const float md = sd[b] * inv_n;
+            const float mean = sh[b] + md;
+            const float rstd = 1.0f / sqrtf(fmaxf(sq[b] * inv_n - md * md, 0.f) + S.in.eps);
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const bool ok = b < a.B && lt + TS * i < nvec;
+#pragma unroll
+                for (int e = 0; e < E; ++e) raw[b][i][e] = ok ? (raw[b][i][e] - mean) * rstd : 0.f;
+                ys[b][i].set(raw[b][i], 0);
+            }
+        }
     }
-    load_group(qb, base0 + stride + tm);
 
     // One group: dot products on q, then q is refilled with the group two steps ahead
     // before the reduction.  Every team of the block runs the same number of steps (a

@@ -84,7 +84,7 @@ __device__ __forceinline__ void fill_slice(_Float16* ys, float (*mom)[2], const 
 }
 
 __device__ __forceinline__ bool same_input(const RowInput& p, const RowInput& q) {
-    return p.y == q.y && p.x == q.x && p.stats == q.stats && p.ntiles == q.ntiles && p.eps == q.eps;
+    return same_row_input(p, q);
 }
 
 template <int BT>
@@ -240,7 +240,8 @@ long long mfma_partial_floats(int B, long long max_rows, int max_cols) {
 hipError_t launch_gemv_mfma(const GemvArgs& a, float* partial, hipStream_t s) {
     if (a.B < 1 || a.B > kMaxBatchMfma || a.cols % kMK != 0 || !partial) return hipErrorInvalidValue;
     for (int i = 0; i < a.nseg; ++i)
-        if (!a.seg[i].in.y && (!a.seg[i].in.x || !a.seg[i].in.stats)) return hipErrorInvalidValue;
+        if (!a.seg[i].in.y && (!a.seg[i].in.x || !a.seg[i].in.stats || a.seg[i].in.own_stats))
+            return hipErrorInvalidValue;
     MfmaPlan p{};
     p.bpad = bpad_of(a.B);
     slice_shape(a.cols, p.bpad, &p.S, &p.kc);

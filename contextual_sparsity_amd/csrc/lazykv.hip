@@ -169,7 +169,7 @@ __global__ __launch_bounds__(kLazyThreads) void lazy_kv_kernel(LazyKvArgs a) {
 hipError_t launch_lazy_kv(bool f16, const LazyKvArgs& a, hipStream_t s) {
     // an empty head list (top-k with k = 0) still saves the step's input and carries the
     // valid lengths over; there is nothing to catch up
-    if (a.B < 1 || a.d < 1 || a.h < 1 || a.n < 0 || a.n >= a.n_cap || a.heads.cap < 0)
+    if (a.B < 1 || a.d < 1 || a.h < 1 || a.n < 0 || a.n >= a.n_cap || a.heads.cap < 0 || a.in.own_stats)
         return hipErrorInvalidValue;
     const long long tiles = (long long)a.heads.cap * 2 * a.dh / kRowTile;  // dh % 4 == 0
     const dim3 grid((unsigned)(a.B + 1 + tiles));

@@ -34,7 +34,8 @@ EXPORTS = [
     "dejavu_dense_mlp",
     "dejavu_sparse_mha", "dejavu_dense_mha", "dejavu_neuron_norms", "dejavu_head_norms",
     "dejavu_sparse_layer", "dejavu_stack_decode", "dejavu_poll_device_error",
-    "dejavu_set_mfma_min_batch", "dejavu_gather_rows", "dejavu_profile_kernel", "dejavu_profile_count",
+    "dejavu_set_mfma_min_batch", "dejavu_set_deterministic", "dejavu_gather_rows", "dejavu_profile_kernel",
+    "dejavu_profile_count",
     "dejavu_read_probe", "dejavu_last_error", "dejavu_version",
 ]
 
@@ -103,6 +104,7 @@ def lib() -> ctypes.CDLL:
                                     _I, ctypes.POINTER(djv_trace), _P, _SZ, _P],
             "dejavu_poll_device_error": [_P, ctypes.POINTER(ctypes.c_uint32)],
             "dejavu_set_mfma_min_batch": [_I, ctypes.POINTER(_I)],
+            "dejavu_set_deterministic": [_I, ctypes.POINTER(_I)],
             "dejavu_gather_rows": [_I, _I, _I, _I, _P, _P, _P, _I, _P, _P],
             "dejavu_profile_kernel": [_I, ctypes.POINTER(_P), _I],
             "dejavu_profile_count": [ctypes.POINTER(_I)],
@@ -320,6 +322,13 @@ def dejavu_set_mfma_min_batch(b: int) -> int:
     prev = _I(0)
     _check(lib().dejavu_set_mfma_min_batch(int(b), ctypes.byref(prev)))
     return prev.value
+
+
+def dejavu_set_deterministic(on: bool) -> bool:
+    """Bitwise-reproducible lookahead stacks on or off (see the header); returns the old value."""
+    prev = _I(0)
+    _check(lib().dejavu_set_deterministic(int(bool(on)), ctypes.byref(prev)))
+    return bool(prev.value)
 
 
 def dejavu_profile_kernel(family, events=None) -> None:

@@ -316,6 +316,14 @@ djv_status dejavu_sparse_layer(const djv_model* m, const djv_layer* layer, float
  *   computes; layer 0's sets are predicted first from LN(x_0).  The overlap is inside
  *   launches on the one stream: the predictor weights stream in the same launches as
  *   layer l's weights and each selection runs in a side block of a later launch.
+ *   With lookahead, B <= DJV_MAX_VALU_BATCH (vector ALU), no lazy K/V buffers and
+ *   dejavu_set_deterministic off (the default), the residual stream stays in x between
+ *   launches: the attention and MLP outputs are added to it with fp32 atomics, so no
+ *   reduction launch follows either output projection, and the kernels that read LN(x)
+ *   compute its moments themselves.  The order of those additions depends on scheduling,
+ *   so two runs may differ in the last bits of x (and, through them, in the sets of later
+ *   layers where two scores nearly tie); with dejavu_set_deterministic(1) the partial sums
+ *   are reduced in a fixed order instead and every run gives the same bits.
  *   lookahead = 0: each layer as dejavu_sparse_layer.
  *   dense = 1: every layer dense (all heads and neurons, no predictor).
  *   layers: host array of L descriptors.  Everything is enqueued on `stream`; nothing is
@@ -348,6 +356,16 @@ djv_status dejavu_poll_device_error(void* stream, uint32_t* flags);
  *   row-axpy coefficients to fp16.
  * ------------------------------------------------------------------------------------ */
 djv_status dejavu_set_mfma_min_batch(int b, int* previous);
+
+/* --------------------------------------------------------------------------------------
+ * dejavu_set_deterministic -- on = 1: every call gives the same bits for the same inputs
+ *   (the lookahead stack reduces its output-projection partial sums in a fixed order, one
+ *   extra launch after each projection).  on = 0 (default): the lookahead stack adds them
+ *   to the residual stream with atomics (see dejavu_stack_decode).  Other calls are always
+ *   reproducible.  *previous (host, may be NULL) receives the value replaced; DJV_EINVAL
+ *   unless on is 0 or 1.  Process-wide, read once per call when it plans its launches.
+ * ------------------------------------------------------------------------------------ */
+djv_status dejavu_set_deterministic(int on, int* previous);
 
 /* --------------------------------------------------------------------------------------
  * Benchmark hook.  dejavu_profile_kernel(family, events, capacity): from now on, every

@@ -44,6 +44,18 @@ def assert_close(got, ref, tol: float, ctx=None) -> None:
             (ctx, "element", worst, "rms", rms, "at", np.unravel_index(int(np.abs(g - r).argmax()), g.shape))
 
 
+class deterministic:
+    """Context: lookahead stacks with fixed-order reductions (bitwise reproducible)."""
+
+    def __enter__(self):
+        self.prev = dj.dejavu_set_deterministic(True)
+        return self
+
+    def __exit__(self, *exc):
+        dj.dejavu_set_deterministic(self.prev)
+        return False
+
+
 def host(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().numpy()
 

@@ -226,6 +226,17 @@ def test_mfma_min_batch_setting():
         assert dj.dejavu_set_mfma_min_batch(old) in (1, dj.DJV_MAX_VALU_BATCH + 1)
 
 
+def test_deterministic_setting():
+    f = dj.lib().dejavu_set_deterministic
+    assert f(2, None) == dj.DJV_EINVAL and f(-1, None) == dj.DJV_EINVAL
+    old = dj.dejavu_set_deterministic(True)
+    assert old is False
+    try:
+        assert dj.dejavu_set_deterministic(True) is True
+    finally:
+        assert dj.dejavu_set_deterministic(old) is True
+
+
 def test_gather_rows_argument_errors():
     g = dj.dejavu_gather_rows
     ok = dict(wt=dj.DJV_F16, rpu=1, cols=768, units=3072, W=A, idx=A, count=A, cap=154, out=A)

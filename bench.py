@@ -33,7 +33,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
 HEADLINE_METRIC = "sparse decode-layer µs and HBM GB/s (% of peak), OPT-175B shape, 5% MLP/20% heads"
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qkv_p1_launch_opt175b_traffic.txt")
-KERNEL_SOURCES = ["common.hpp", "gemv.hpp", "select.hpp", "attn.hpp", "gemv_f16_side.hip"]
+KERNEL_SOURCES = ["common.hpp", "gemv.hpp", "select.hpp", "attn.hpp", "gemv_f16_side.hip", "gemv_own_f16.hip"]
 
 
 def kernel_sources_sha():

@@ -39,7 +39,8 @@ SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=und
              "-Xarch_host", "-g"]
 
 SOURCES = ["api.cpp", "gemv.hip", "gemv_f16.hip", "gemv_f16_side.hip", "gemv_f32.hip",
-           "gemv_f32_side.hip", "gemv_dyn_f16.hip", "gemv_dyn_f32.hip", "gemv_mfma.hip", "gather.hip",
+           "gemv_f32_side.hip", "gemv_dyn_f16.hip", "gemv_dyn_f32.hip", "gemv_own_f16.hip", "gemv_own_f32.hip",
+           "gemv_own_dyn_f16.hip", "gemv_own_dyn_f32.hip", "gemv_mfma.hip", "gather.hip",
            "axpy.hip", "attn.hip", "select.hip", "norms.hip", "lazykv.hip", "misc.hip"]
 ARCH = "gfx950"
 

@@ -12,6 +12,32 @@ hipError_t launch_gemv_f32_dyn(const GemvArgs& a, hipStream_t s);
 hipError_t launch_gemv_f32_side_dyn(const GemvArgs& a, hipStream_t s);
 hipError_t launch_gemv_f16_dyn(const GemvArgs& a, hipStream_t s);
 hipError_t launch_gemv_f16_side_dyn(const GemvArgs& a, hipStream_t s);
+hipError_t launch_gemv_f32_own(const GemvArgs& a, hipStream_t s);
+hipError_t launch_gemv_f32_side_own(const GemvArgs& a, hipStream_t s);
+hipError_t launch_gemv_f16_own(const GemvArgs& a, hipStream_t s);
+hipError_t launch_gemv_f16_side_own(const GemvArgs& a, hipStream_t s);
+hipError_t launch_gemv_f32_dyn_own(const GemvArgs& a, hipStream_t s);
+hipError_t launch_gemv_f32_side_dyn_own(const GemvArgs& a, hipStream_t s);
+hipError_t launch_gemv_f16_dyn_own(const GemvArgs& a, hipStream_t s);
+hipError_t launch_gemv_f16_side_dyn_own(const GemvArgs& a, hipStream_t s);
+
+namespace {
+// The four launch forms of one weight dtype and input kind.
+using LaunchFn = hipError_t (*)(const GemvArgs&, hipStream_t);
+struct Forms {
+    LaunchFn plain, side, dyn, side_dyn;
+};
+Forms forms(bool f16, bool own) {
+    if (f16) {
+        if (own) return {launch_gemv_f16_own, launch_gemv_f16_side_own, launch_gemv_f16_dyn_own,
+                         launch_gemv_f16_side_dyn_own};
+        return {launch_gemv_f16, launch_gemv_f16_side, launch_gemv_f16_dyn, launch_gemv_f16_side_dyn};
+    }
+    if (own) return {launch_gemv_f32_own, launch_gemv_f32_side_own, launch_gemv_f32_dyn_own,
+                     launch_gemv_f32_side_dyn_own};
+    return {launch_gemv_f32, launch_gemv_f32_side, launch_gemv_f32_dyn, launch_gemv_f32_side_dyn};
+}
+}  // namespace
 
 static hipError_t launch_valu(bool f16, const GemvArgs& a, hipStream_t s);
 
@@ -46,6 +72,12 @@ hipError_t launch_gemv(bool f16, const GemvArgs& a, hipStream_t s) {
 }
 
 static hipError_t launch_valu(bool f16, const GemvArgs& a, hipStream_t s) {
+    // LN(x) with moments summed by the kernel runs in its own instantiations: all segments
+    // of a launch read the same kind of input
+    const bool own = !a.seg[0].in.y && a.seg[0].in.own_stats;
+    for (int i = 1; i < a.nseg; ++i)
+        if ((!a.seg[i].in.y && a.seg[i].in.own_stats) != own) return hipErrorInvalidValue;
+    const Forms F = forms(f16, own);
     bool long_rows = false;
     for (int i = 0; i < a.nside; ++i) long_rows = long_rows || a.side[i].n_out > kShortRows;
     if (long_rows && (a.nattn > 0 || a.B > 1)) {
@@ -55,17 +87,12 @@ static hipError_t launch_valu(bool f16, const GemvArgs& a, hipStream_t s) {
         if (e != hipSuccess) return e;
         GemvArgs b = a;
         b.nside = 0;
-        if (a.dyn) return f16 ? launch_gemv_f16_dyn(b, s) : launch_gemv_f32_dyn(b, s);
-        return f16 ? launch_gemv_f16(b, s) : launch_gemv_f32(b, s);
+        return a.dyn ? F.dyn(b, s) : F.plain(b, s);
     }
-    if (a.dyn && (long_rows || a.nside == 0)) {
-        if (f16) return long_rows ? launch_gemv_f16_side_dyn(a, s) : launch_gemv_f16_dyn(a, s);
-        return long_rows ? launch_gemv_f32_side_dyn(a, s) : launch_gemv_f32_dyn(a, s);
-    }
+    if (a.dyn && (long_rows || a.nside == 0)) return long_rows ? F.side_dyn(a, s) : F.dyn(a, s);
     GemvArgs b = a;
     b.dyn = false;  // short-row side selections run in the static form
-    if (f16) return long_rows ? launch_gemv_f16_side(b, s) : launch_gemv_f16(b, s);
-    return long_rows ? launch_gemv_f32_side(b, s) : launch_gemv_f32(b, s);
+    return long_rows ? F.side(b, s) : F.plain(b, s);
 }
 
 }  // namespace djv

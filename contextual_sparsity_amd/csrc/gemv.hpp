@@ -202,7 +202,9 @@ struct Group {
     int sg, lg;
 };
 
-template <typename T, int TS, int NV, int NB, int G, int MODE, bool DYN>
+// OWN: the input is LN(x) of an x accumulated in place, its moments summed here (a
+// separate instantiation, so the kernels of the other inputs keep their registers).
+template <typename T, int TS, int NV, int NB, int G, int MODE, bool DYN, bool OWN>
 __global__ __launch_bounds__(BlockOf<MODE>::value) void gemv_kernel(GemvArgs a) {
     constexpr int kThreads = BlockOf<MODE>::value;
     int bid = (int)blockIdx.x;
@@ -230,10 +232,10 @@ __global__ __launch_bounds__(BlockOf<MODE>::value) void gemv_kernel(GemvArgs a) 
     constexpr int NT = kThreads / TS;
     constexpr int NW = TS / kWave;  // waves per team
     __shared__ float red[2][NT][NW][G * NB];
-    __shared__ float mom[2][NT][NW][NB];  // wave sums of the row moments (own_stats)
-    // several teams of several waves (1024-thread blocks): with own_stats the block loads
-    // and normalises the row once, into LDS, where every team reads its slice
-    constexpr bool kCoop = NT > 1 && NW > 1;
+    // OWN with several teams of several waves (1024-thread blocks): the block loads and
+    // normalises the row once, into LDS, where every team reads its slices
+    constexpr bool kCoop = OWN && NT > 1 && NW > 1;
+    __shared__ float mom[2][OWN ? NT : 1][OWN ? NW : 1][NB];  // wave sums of the row moments
     __shared__ YSlice<T> ylds[kCoop ? kMaxRowVecs : 1];
     __shared__ float momc[2][kCoop ? kThreads / kWave : 1];
 
@@ -340,8 +342,7 @@ __global__ __launch_bounds__(BlockOf<MODE>::value) void gemv_kernel(GemvArgs a) 
 
     // this thread's slice of every batch row (loads clamped in range, then masked)
     YSlice<T> ys[NB][NV];
-    const bool own = !S.in.y && S.in.own_stats;  // uniform over the block
-    if (!own) {
+    if constexpr (!OWN) {
         float raw[NB][NV][8];
 #pragma unroll
         for (int b = 0; b < NB; ++b)
@@ -585,12 +586,12 @@ __global__ __launch_bounds__(BlockOf<MODE>::value) void gemv_kernel(GemvArgs a) 
     }
 }
 
-template <typename T, int TS, int NV, int NB, int G, int MODE, bool DYN>
+template <typename T, int TS, int NV, int NB, int G, int MODE, bool DYN, bool OWN>
 int blocks_per_cu() {
     static const int occ = [] {
         int n = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &n, reinterpret_cast<const void*>(&gemv_kernel<T, TS, NV, NB, G, MODE, DYN>),
+                &n, reinterpret_cast<const void*>(&gemv_kernel<T, TS, NV, NB, G, MODE, DYN, OWN>),
                 BlockOf<MODE>::value, 0) !=
                 hipSuccess ||
             n < 1)
@@ -605,10 +606,10 @@ constexpr int kOversub = 1;
 
 // Shares the resident blocks among the segments in proportion to their groups of rows
 // (at least one each) and launches.
-template <typename T, int TS, int NV, int NB, int G, int MODE, bool DYN>
+template <typename T, int TS, int NV, int NB, int G, int MODE, bool DYN, bool OWN>
 hipError_t launch_shape(GemvArgs a, hipStream_t s) {
     constexpr int NT = BlockOf<MODE>::value / TS;
-    const int slots = blocks_per_cu<T, TS, NV, NB, G, MODE, DYN>() * device_cus() * kOversub;
+    const int slots = blocks_per_cu<T, TS, NV, NB, G, MODE, DYN, OWN>() * device_cus() * kOversub;
     if (MODE != 1) a.nattn = 0;
     if (MODE == 0) a.nside = 0;
     // the prefix blocks (attention chunks, selections) are short; when they fill most of
@@ -635,16 +636,16 @@ hipError_t launch_shape(GemvArgs a, hipStream_t s) {
     }
     dim3 grid(total + nprefix);
     prof_begin(a.prof, s);
-    hipLaunchKernelGGL((gemv_kernel<T, TS, NV, NB, G, MODE, DYN>), grid, dim3(BlockOf<MODE>::value), 0, s, a);
+    hipLaunchKernelGGL((gemv_kernel<T, TS, NV, NB, G, MODE, DYN, OWN>), grid, dim3(BlockOf<MODE>::value), 0, s, a);
     prof_end(a.prof, s);
     return hipGetLastError();
 }
 
-template <typename T, int TS, int NB, int MODE, bool DYN>
+template <typename T, int TS, int NB, int MODE, bool DYN, bool OWN>
 hipError_t dispatch_nv(const GemvArgs& a, int nv, hipStream_t s) {
 #define DJV_GEMV_CASE(NVV, GG) \
     case NVV:                  \
-        return launch_shape<T, TS, NVV, NB, GG, MODE, DYN>(a, s);
+        return launch_shape<T, TS, NVV, NB, GG, MODE, DYN, OWN>(a, s);
     if constexpr (TS == 64) {
         switch (nv) {
             DJV_GEMV_CASE(1, 4)
@@ -686,8 +687,9 @@ hipError_t dispatch_nv(const GemvArgs& a, int nv, hipStream_t s) {
 #undef DJV_GEMV_CASE
 }
 
-// Chooses the team size, vectors per thread and rows per team, and launches.
-template <typename T, int MODE, bool DYN = false>
+// Chooses the team size, vectors per thread and rows per team, and launches.  OWN: every
+// segment reads LN(x) with own_stats (checked by the caller).
+template <typename T, int MODE, bool DYN = false, bool OWN = false>
 hipError_t dispatch(const GemvArgs& a, hipStream_t s) {
     constexpr int E = WTraits<T>::kPerVec;
     if (a.nseg < 1 || a.nseg > kMaxSeg || a.nside < 0 || a.nside > kMaxSide) return hipErrorInvalidValue;
@@ -700,16 +702,16 @@ hipError_t dispatch(const GemvArgs& a, hipStream_t s) {
         // long-row side selections are compiled for one batch row only (the launcher runs
         // them separately otherwise)
         if (nb != 1) return hipErrorInvalidValue;
-        return small ? dispatch_nv<T, 64, 1, MODE, DYN>(a, nv, s) : dispatch_nv<T, 256, 1, MODE, DYN>(a, nv, s);
+        return small ? dispatch_nv<T, 64, 1, MODE, DYN, OWN>(a, nv, s) : dispatch_nv<T, 256, 1, MODE, DYN, OWN>(a, nv, s);
     } else {
         if (small) {
-            if (nb == 1) return dispatch_nv<T, 64, 1, MODE, DYN>(a, nv, s);
-            if (nb == 2) return dispatch_nv<T, 64, 2, MODE, DYN>(a, nv, s);
-            return dispatch_nv<T, 64, 4, MODE, DYN>(a, nv, s);
+            if (nb == 1) return dispatch_nv<T, 64, 1, MODE, DYN, OWN>(a, nv, s);
+            if (nb == 2) return dispatch_nv<T, 64, 2, MODE, DYN, OWN>(a, nv, s);
+            return dispatch_nv<T, 64, 4, MODE, DYN, OWN>(a, nv, s);
         }
-        if (nb == 1) return dispatch_nv<T, 256, 1, MODE, DYN>(a, nv, s);
-        if (nb == 2) return dispatch_nv<T, 256, 2, MODE, DYN>(a, nv, s);
-        return dispatch_nv<T, 256, 4, MODE, DYN>(a, nv, s);
+        if (nb == 1) return dispatch_nv<T, 256, 1, MODE, DYN, OWN>(a, nv, s);
+        if (nb == 2) return dispatch_nv<T, 256, 2, MODE, DYN, OWN>(a, nv, s);
+        return dispatch_nv<T, 256, 4, MODE, DYN, OWN>(a, nv, s);
     }
 }
 

@@ -86,19 +86,21 @@ __device__ __forceinline__ void load_raw(const RowInput& in, int cols, int b, in
 }
 
 // LayerNorm moments of row b from its slice statistics; each lane loads its (at most
-// four) slices at once.  cols <= 16384, so ntiles <= 256.
-__device__ __forceinline__ void row_moments(const RowInput& in, int cols, int b, float& mean,
-                                            float& rstd) {
+// four) slices at once.  cols <= 16384, so ntiles <= 256.  In two parts, so a caller can
+// place other loads between the statistics' loads and their use.
+__device__ __forceinline__ void row_moments_load(const RowInput& in, int cols, int b, float2 (&v)[4],
+                                                 float (&nt)[4]) {
     const int lane = threadIdx.x % kWave;
     const float2* st = in.stats + (size_t)b * in.ntiles;
-    float2 v[4];
-    float nt[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int t = lane + kWave * q;
         v[q] = st[min(t, in.ntiles - 1)];
         nt[q] = t < in.ntiles ? (float)min(kLnTile, cols - t * kLnTile) : 0.f;
     }
+}
+__device__ __forceinline__ void row_moments_finish(const RowInput& in, int cols, const float2 (&v)[4],
+                                                   const float (&nt)[4], float& mean, float& rstd) {
     float s = 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) s = fmaf(nt[q], v[q].x, s);
@@ -111,6 +113,13 @@ __device__ __forceinline__ void row_moments(const RowInput& in, int cols, int b,
     }
     mean = m;
     rstd = 1.0f / sqrtf(wave_sum(qs) / (float)cols + in.eps);
+}
+__device__ __forceinline__ void row_moments(const RowInput& in, int cols, int b, float& mean,
+                                            float& rstd) {
+    float2 v[4];
+    float nt[4];
+    row_moments_load(in, cols, b, v, nt);
+    row_moments_finish(in, cols, v, nt, mean, rstd);
 }
 
 // What a group's weight loads need of its segment, and what its stores need: small
@@ -338,11 +347,16 @@ __global__ __launch_bounds__(BlockOf<MODE>::value) void gemv_kernel(GemvArgs a) 
     const int base0 = bid * NT;
     if (base0 >= groups) return;  // uniform over the block
     Group<G, NV> qa, qb;
-    load_group(qa, base0 + tm);
 
-    // this thread's slice of every batch row (loads clamped in range, then masked)
+    // this thread's slice of every batch row (loads clamped in range, then masked).  At one
+    // batch row the activation (and statistics) loads go out before the first group's
+    // weights: the load counter is in order, so a wait for activations requested after the
+    // weights would wait for the weights too, and the team computes nothing before its
+    // activations.  (With more rows the statistics of all rows held across the weight
+    // requests would cost occupancy; there the weights go first.)
     YSlice<T> ys[NB][NV];
     if constexpr (!OWN) {
+        if constexpr (NB > 1) load_group(qa, base0 + tm);
         float raw[NB][NV][8];
 #pragma unroll
         for (int b = 0; b < NB; ++b)
@@ -351,10 +365,19 @@ __global__ __launch_bounds__(BlockOf<MODE>::value) void gemv_kernel(GemvArgs a) 
                 const int v = min(lt + TS * i, nvec - 1);
                 load_raw<T>(S.in, a.cols, min(b, a.B - 1), v * E, raw[b][i]);
             }
+        float2 stv[4];
+        float ntv[4];
+        if constexpr (NB == 1) {
+            if (!S.in.y) row_moments_load(S.in, a.cols, 0, stv, ntv);
+            load_group(qa, base0 + tm);
+        }
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             float mean = 0.f, rstd = 1.f;
-            if (!S.in.y) row_moments(S.in, a.cols, min(b, a.B - 1), mean, rstd);
+            if (!S.in.y) {
+                if constexpr (NB == 1) row_moments_finish(S.in, a.cols, stv, ntv, mean, rstd);
+                else row_moments(S.in, a.cols, min(b, a.B - 1), mean, rstd);
+            }
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
                 const bool ok = b < a.B && lt + TS * i < nvec;
@@ -368,15 +391,14 @@ __global__ __launch_bounds__(BlockOf<MODE>::value) void gemv_kernel(GemvArgs a) 
         // own_stats, several teams of several waves: the block's threads share the row's
         // vectors (at most KV each), sum the row's moments over all of the block's waves
         // (as the per-team form below), and leave the normalised row in LDS, where every
-        // team reads its slices.  The second group's weights are requested before the
-        // barrier, so they are in flight while the moments are formed.
+        // team reads its slices.  Both groups' weights are requested right after the
+        // activations, so they are in flight while the moments are formed.
         static_assert(!kCoop || NB == 1, "the block-wide prologue serves one batch row");
         constexpr int KV = (NV * TS + kThreads - 1) / kThreads;
         float raw[KV][8];
 #pragma unroll
         for (int k = 0; k < KV; ++k)
             load_raw<T>(S.in, a.cols, 0, min(tid + kThreads * k, nvec - 1) * E, raw[k]);
-        load_group(qb, base0 + stride + tm);
         const float sh = S.in.x[0];
         float t1 = 0.f, t2 = 0.f;
 #pragma unroll
@@ -387,6 +409,11 @@ __global__ __launch_bounds__(BlockOf<MODE>::value) void gemv_kernel(GemvArgs a) 
                 t1 += dv;
                 t2 = fmaf(dv, dv, t2);
             }
+        // the sums (so the wait for the activations) before the weight requests: a wait
+        // placed after them would also wait for weights, the load counter being in order
+        asm volatile("" : : "v"(t1), "v"(t2) : "memory");
+        load_group(qa, base0 + tm);
+        load_group(qb, base0 + stride + tm);
         t1 = wave_sum(t1);
         t2 = wave_sum(t2);
         const int wb = tid / kWave;
@@ -429,8 +456,8 @@ __global__ __launch_bounds__(BlockOf<MODE>::value) void gemv_kernel(GemvArgs a) 
         // the deviations d = x - x[0] from the row's first element, mean = x[0] + sum(d)/n
         // and variance = (sum(d^2) - sum(d)^2/n)/n (the shift keeps the squares on the
         // scale of the spread rather than of the mean); wave sums, then (several waves per
-        // team) a sum over the team's waves through LDS, one barrier.  The second group's
-        // weights are requested before it.
+        // team) a sum over the team's waves through LDS, one barrier.  Both groups' weights
+        // are requested right after the activations, before it.
         float raw[NB][NV][8];
 #pragma unroll
         for (int b = 0; b < NB; ++b)
@@ -439,7 +466,6 @@ __global__ __launch_bounds__(BlockOf<MODE>::value) void gemv_kernel(GemvArgs a) 
                 const int v = min(lt + TS * i, nvec - 1);
                 load_raw<T>(S.in, a.cols, min(b, a.B - 1), v * E, raw[b][i]);
             }
-        load_group(qb, base0 + stride + tm);
         float sd[NB], sq[NB], sh[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
@@ -453,8 +479,18 @@ __global__ __launch_bounds__(BlockOf<MODE>::value) void gemv_kernel(GemvArgs a) 
                     t1 += dv;
                     t2 = fmaf(dv, dv, t2);
                 }
-            sd[b] = wave_sum(t1);
-            sq[b] = wave_sum(t2);
+            sd[b] = t1;
+            sq[b] = t2;
+            // the sums (so the wait for the activations) before the weight requests: a wait
+            // placed after them would also wait for weights, the load counter being in order
+            asm volatile("" : : "v"(t1), "v"(t2) : "memory");
+        }
+        load_group(qa, base0 + tm);
+        load_group(qb, base0 + stride + tm);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            sd[b] = wave_sum(sd[b]);
+            sq[b] = wave_sum(sq[b]);
         }
         if constexpr (NW > 1) {
             if (ln == 0) {

@@ -27,6 +27,10 @@
 namespace djv {
 namespace {
 
+// A 16-byte zero vector: loads of absent rows read it, so every weight load is issued
+// unconditionally.
+static __device__ const Vec16 g_zero16 = {};
+
 constexpr int kUnroll = 8;      // rows in flight per wave
 constexpr int kWavesPerBlock = 4;
 constexpr int kThreads = 256;
@@ -49,14 +53,100 @@ __device__ __forceinline__ int chunk_rows(const AxpyArgs& a, int rows) {
 // the sums taken in chunk order ([NOTES "Sparsified Attention"]: H_i = D_i^{-1} exp(.) X
 // W_i^V, the chunks' maxima cancelling between numerator and D_i).  A chunk of at most dh
 // rows touches at most two unit slots; their (m, l) go through LDS first.
+//
+// The staging of a chunk (row numbers and coefficients, plain or merged) is in two parts:
+// stage_load issues the loads of each thread's first row and (m, l) entry, before the
+// chunk's first weight requests, and stage_finish, after them, waits for those loads only
+// (the vector load counter completes in issue order, so loads issued after the weights
+// would also wait for the weights), merges, and fills LDS.
 template <int NB>
-__device__ __forceinline__ void stage_attention(const AxpyArgs& a, int r0, int nr, float* cf_s,
-                                                int* row_s, float* wm, float* wl, float* inv) {
-    const int tid = threadIdx.x, dh = a.rpu, nck = a.attn_nchunk, cap = a.list.cap;
+struct StageRegs {
+    static constexpr int kPre = 32 / NB;  // attention chunks whose accumulators are preloaded
+    int unit;                             // index entry of this thread's first row (unchecked)
+    float cf[NB];                         // its coefficients (plain rows)
+    float m, l;                           // entry tid of [b][h][ch] (attention)
+    float av[NB][kPre];                   // its row's chunk accumulators (attention)
+};
+
+template <int NB>
+__device__ __forceinline__ void stage_load(const AxpyArgs& a, int r0, int nr, StageRegs<NB>& R) {
+    constexpr int kPre = StageRegs<NB>::kPre;
+    const int tid = threadIdx.x;
+    // only threads with a row (or an (m, l) entry) load, at clamped (in-range) addresses,
+    // and no memory operation with a side effect sits in these branches; stage_finish
+    // masks what does not belong to the chunk
+    const int r = r0 + min(tid, nr - 1);  // this thread's first row (nr >= 1)
+    const int u = r / a.rpu;               // < count <= cap
+    const int bmax = a.B - 1;
+    if (tid < nr) R.unit = a.list.idx ? a.list.idx[u] : u;
+    if (a.attn_part) {
+        const int dh = a.rpu, nck = a.attn_nchunk, cap = a.list.cap;
+        const int u0 = r0 / dh;
+        const size_t stride = (size_t)dh + 2;
+        if (tid < NB * 2 * nck) {  // entry [b][h][ch]
+            const int ch = tid % nck, h = (tid / nck) % 2, b = min(tid / (2 * nck), bmax);
+            const float* pm = a.attn_part + (((size_t)b * cap + min(u0 + h, cap - 1)) * nck + ch) * stride;
+            R.m = pm[0];
+            R.l = pm[1];
+        }
+        if (nck <= kPre && tid < nr) {
+            const int c = r - u * dh;
+#pragma unroll
+            for (int b2 = 0; b2 < NB; ++b2) {
+                const float* pp = a.attn_part + ((size_t)min(b2, bmax) * cap + u) * nck * stride + 2 + c;
+#pragma unroll
+                for (int k = 0; k < kPre; ++k) R.av[b2][k] = pp[(size_t)min(k, nck - 1) * stride];
+            }
+        }
+    } else if (tid < nr) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) R.cf[b] = a.coef[(size_t)min(b, bmax) * a.ldc + r];
+    }
+}
+
+template <int NB>
+__device__ __forceinline__ void stage_finish(const AxpyArgs& a, int r0, int nr, const StageRegs<NB>& R,
+                                             float* cf_s, int* row_s, float* dyn_attn) {
+    constexpr int kPre = StageRegs<NB>::kPre;
+    const int tid = threadIdx.x;
+    // the first row's unit, checked as unit_of checks it
+    int unit = tid < nr ? R.unit : -1;
+    if (tid < nr && a.list.idx && (unit < 0 || unit >= a.list.units)) {
+        set_flag(a.flags, kFlagBadIndex);
+        unit = -1;
+    }
+    if (!a.attn_part) {
+        if (tid < nr) {
+            const int r = r0 + tid;
+            row_s[tid] = unit < 0 ? -1 : unit * a.rpu + (r - (r / a.rpu) * a.rpu);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) cf_s[b * a.rows_per_chunk + tid] = (unit >= 0 && b < a.B) ? R.cf[b] : 0.f;
+        }
+        for (int i = tid + kThreads; i < nr; i += kThreads) {
+            const int r = r0 + i;
+            const int u = r / a.rpu, sub = r - u * a.rpu;
+            const int unit = unit_of(a.list, u, a.flags);
+            row_s[i] = unit < 0 ? -1 : unit * a.rpu + sub;
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                cf_s[b * a.rows_per_chunk + i] = (unit >= 0 && b < a.B) ? a.coef[(size_t)b * a.ldc + r] : 0.f;
+        }
+        return;
+    }
+    const int dh = a.rpu, nck = a.attn_nchunk, cap = a.list.cap;
     const int u0 = r0 / dh;
     const int nh = (r0 + nr - 1) / dh - u0 + 1;  // 1 or 2
     const size_t stride = (size_t)dh + 2;
-    for (int i = tid; i < NB * 2 * nck; i += kThreads) {  // [b][h][ch]
+    float* wm = dyn_attn;
+    float* wl = wm + NB * 2 * nck;
+    float* inv = wl + NB * 2 * nck;
+    if (tid < NB * 2 * nck) {
+        const int h = (tid / nck) % 2, b = tid / (2 * nck);
+        const bool ok = b < a.B && h < nh;
+        wm[tid] = ok ? R.m : -INFINITY;
+        wl[tid] = ok ? R.l : 0.f;
+    }
+    for (int i = tid + kThreads; i < NB * 2 * nck; i += kThreads) {
         const int ch = i % nck, h = (i / nck) % 2, b = i / (2 * nck);
         float m = -INFINITY, l = 0.f;
         if (b < a.B && h < nh) {
@@ -82,6 +172,28 @@ __device__ __forceinline__ void stage_attention(const AxpyArgs& a, int r0, int n
         inv[tid] = L;
     }
     __syncthreads();
+    if (nck <= kPre) {
+        // the preloaded accumulators of this thread's row
+        if (tid < nr) {
+            const int r = r0 + tid;
+            const int u = r / dh, c = r - u * dh, h = u - u0;
+            row_s[tid] = unit < 0 ? -1 : unit * dh + c;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                float v = 0.f;
+                if (unit >= 0 && b < a.B) {
+                    const float* w = wm + (b * 2 + h) * nck;
+                    float acc = 0.f;
+#pragma unroll
+                    for (int k = 0; k < kPre; ++k)
+                        if (k < nck) acc = fmaf(R.av[b][k], w[k], acc);
+                    v = acc / inv[b * 2 + h];
+                }
+                cf_s[b * a.rows_per_chunk + tid] = v;
+            }
+        }
+        return;
+    }
     for (int i = tid; i < nr; i += kThreads) {
         const int r = r0 + i;
         const int u = r / dh, c = r - u * dh, h = u - u0;
@@ -136,11 +248,19 @@ __global__ __launch_bounds__(kThreads) void axpy_partial_kernel(AxpyArgs a) {
     const char* Wb = reinterpret_cast<const char*>(a.W);
     const size_t row_bytes = (size_t)a.cols * sizeof(T);
 
-    // the wave's first kUnroll rows (uniform over the wave: scalar index loads) are
-    // requested before the coefficients are staged, so their latency overlaps the staging
-    // (and the attention merge)
+    // the staging loads first, then the wave's first kUnroll rows (uniform over the wave:
+    // scalar index loads), whose latency overlaps the rest of the staging (and the
+    // attention merge)
+    StageRegs<NB> sr;
+    stage_load<NB>(a, r0, nr, sr);
+    // (unconditional: an absent row reads a static zero vector, and a bad index is flagged
+    // by the staging's check of the same rows, so no branch with a memory operation sits
+    // between the staging loads and their use, which would make the compiler wait for all
+    // loads in flight there)
     Vec16 w0[kUnroll];
     const int wvu = __builtin_amdgcn_readfirstlane(wv);
+    gchar* zero = reinterpret_cast<gchar*>(reinterpret_cast<uint64_t>(&g_zero16));
+    gchar* Wg = reinterpret_cast<gchar*>(reinterpret_cast<uint64_t>(Wb));
 #pragma unroll
     for (int q = 0; q < kUnroll; ++q) {
         const int i = wvu + q * kWavesPerBlock;
@@ -148,31 +268,14 @@ __global__ __launch_bounds__(kThreads) void axpy_partial_kernel(AxpyArgs a) {
         if (i < nr) {
             const int r = r0 + i;
             const int u = r / a.rpu, sub = r - u * a.rpu;
-            const int unit = unit_of_uniform(a.list, u, a.flags);
-            row = unit < 0 ? -1 : unit * a.rpu + sub;
+            const int unit = a.list.idx ? sload_i32(a.list.idx + u) : u;
+            row = (unit < 0 || unit >= a.list.units) ? -1 : unit * a.rpu + sub;
         }
-        if (row >= 0 && col_ok)
-            w0[q] = ldg16_nt(Wb + (size_t)row * row_bytes + (size_t)v * 16);
-        else
-            w0[q] = Vec16{{0u, 0u, 0u, 0u}};
+        const bool have = row >= 0 && col_ok;
+        w0[q] = ldg16_nt_at(have ? Wg + (size_t)row * row_bytes + (size_t)v * 16 : zero, 0u);
     }
 
-    if (a.attn_part) {
-        float* wm = dyn + (NB + 1) * a.rows_per_chunk;
-        float* wl = wm + NB * 2 * a.attn_nchunk;
-        stage_attention<NB>(a, r0, nr, cf_s, row_s, wm, wl, wl + NB * 2 * a.attn_nchunk);
-    } else {
-        // stage row numbers and coefficients of the chunk
-        for (int i = tid; i < nr; i += kThreads) {
-            const int r = r0 + i;
-            const int u = r / a.rpu, sub = r - u * a.rpu;
-            const int unit = unit_of(a.list, u, a.flags);
-            row_s[i] = unit < 0 ? -1 : unit * a.rpu + sub;
-#pragma unroll
-            for (int b = 0; b < NB; ++b)
-                cf_s[b * a.rows_per_chunk + i] = (unit >= 0 && b < a.B) ? a.coef[(size_t)b * a.ldc + r] : 0.f;
-        }
-    }
+    stage_finish<NB>(a, r0, nr, sr, cf_s, row_s, dyn + (NB + 1) * a.rows_per_chunk);
     __syncthreads();
 
     float acc[NB][E];
@@ -348,7 +451,6 @@ constexpr int kAxLoads = kAxGroup * kAxCols * 2 / 16 / kThreads;  // 16-byte loa
 constexpr int kAxTargetBlocks = 1024;         // about four per compute unit (a constant, so that
                                               // workspace sizes do not depend on the device)
 
-static __device__ const Vec16 g_zero16 = {};
 
 template <int BT>
 __global__ __launch_bounds__(kThreads) void axpy_mfma_kernel(AxpyArgs a) {

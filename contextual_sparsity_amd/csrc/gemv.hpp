@@ -146,6 +146,19 @@ __device__ __forceinline__ Seg pick3(int i, const Seg& s0, const Seg& s1, const 
     return i == 0 ? s0 : (i == 1 ? s1 : s2);
 }
 
+// Stores v (rounded to T) as element i of the T array at global address base.
+template <typename T>
+__device__ __forceinline__ void store_at(uint64_t base, size_t i, float v);
+template <>
+__device__ __forceinline__ void store_at<float>(uint64_t base, size_t i, float v) {
+    *reinterpret_cast<__attribute__((address_space(1))) float*>(base + i * 4) = v;
+}
+template <>
+__device__ __forceinline__ void store_at<__half>(uint64_t base, size_t i, float v) {
+    *reinterpret_cast<__attribute__((address_space(1))) unsigned short*>(base + i * 2) =
+        __half_as_ushort(to_store<__half>(v));
+}
+
 // Writes the result of visited row r (weight unit `unit`, -1 when skipped) for batch row b.
 template <typename T>
 __device__ __forceinline__ void epilogue(const GemvArgs& a, const SegOut& S, int r, int b, float acc,
@@ -167,8 +180,13 @@ __device__ __forceinline__ void epilogue(const GemvArgs& a, const SegOut& S, int
         if (part == 0) {
             S.out[((size_t)b * S.cap + u) * a.dh + c] = acc;
         } else {
-            T* cache = reinterpret_cast<T*>(part == 1 ? a.Kc : a.Vc);
-            cache[(((size_t)b * a.h + unit) * a.n_cap + a.n) * a.dh + c] = to_store<T>(acc);
+            // both cache bases moved to scalar registers and selected there: left to itself the
+            // compiler selects between the two argument fields' addresses and loads the chosen
+            // one with a vector load, whose wait (the load counter is in order) is also a wait
+            // for every weight load in flight
+            const uint64_t kc = reinterpret_cast<uint64_t>(uniform_ptr(a.Kc));
+            const uint64_t vc = reinterpret_cast<uint64_t>(uniform_ptr(a.Vc));
+            store_at<T>(part == 1 ? kc : vc, (((size_t)b * a.h + unit) * a.n_cap + a.n) * a.dh + c, acc);
         }
         break;
     }

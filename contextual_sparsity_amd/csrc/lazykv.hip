@@ -103,21 +103,15 @@ __global__ __launch_bounds__(kLazyThreads) void lazy_kv_kernel(LazyKvArgs a) {
                 for (int t = 0; t < kPosTile; ++t) acc[r][t] = 0.f;
             for (int cv = 0; cv < nvec; cv += kChunkVec) {
                 __syncthreads();  // the previous chunk's readers are done
-                {
-                    Vec16 st[kRowTile * kChunkVec / kLazyThreads];
+                // the tile's weights of the chunk and this wave's inputs of it, all requested
+                // before either is used (one round trip per chunk)
+                Vec16 st[kRowTile * kChunkVec / kLazyThreads];
 #pragma unroll
-                    for (int k = 0; k < kRowTile * kChunkVec / kLazyThreads; ++k) {
-                        const int e = tid + k * kLazyThreads, r = e / kChunkVec, v = e - r * kChunkVec;
-                        st[k] = W[(size_t)r * nvec + min(cv + v, nvec - 1)];  // clamped; unused past the end
-                    }
-#pragma unroll
-                    for (int k = 0; k < kRowTile * kChunkVec / kLazyThreads; ++k) {
-                        const int e = tid + k * kLazyThreads, r = e / kChunkVec, v = e - r * kChunkVec;
-                        wsh[r][v] = st[k];
-                    }
+                for (int k = 0; k < kRowTile * kChunkVec / kLazyThreads; ++k) {
+                    const int e = tid + k * kLazyThreads, r = e / kChunkVec, v = e - r * kChunkVec;
+                    st[k] = W[(size_t)r * nvec + min(cv + v, nvec - 1)];  // clamped; unused past the end
                 }
-                // this wave's inputs of the chunk while the stage completes
-                float4 yv[kPosTile][kLaneVec][E / 4];
+                float yf[kPosTile][kLaneVec][8];
 #pragma unroll
                 for (int t = 0; t < kPosTile; ++t) {
                     const int p = min(p0 + t * kLazyRows, a.n - 1);  // clamped; not stored past n
@@ -126,30 +120,38 @@ __global__ __launch_bounds__(kLazyThreads) void lazy_kv_kernel(LazyKvArgs a) {
                         const int v = min(cv + lane + k * kWave, nvec - 1);
                         const float* y = yb + (size_t)p * a.d + (size_t)v * E;
 #pragma unroll
-                        for (int q = 0; q < E / 4; ++q) yv[t][k][q] = *reinterpret_cast<const float4*>(y + 4 * q);
+                        for (int q = 0; q < E / 4; ++q) {
+                            const float4 f = *reinterpret_cast<const float4*>(y + 4 * q);
+                            yf[t][k][4 * q] = f.x; yf[t][k][4 * q + 1] = f.y;
+                            yf[t][k][4 * q + 2] = f.z; yf[t][k][4 * q + 3] = f.w;
+                        }
                     }
                 }
-                __syncthreads();
-                // branch-free: a vector past the end gets zero inputs and adds exact zeros
-                // (weights are finite)
 #pragma unroll
-                for (int k = 0; k < kLaneVec; ++k) {
-                    const bool ok = cv + lane + k * kWave < nvec;
+                for (int k = 0; k < kRowTile * kChunkVec / kLazyThreads; ++k) {
+                    const int e = tid + k * kLazyThreads, r = e / kChunkVec, v = e - r * kChunkVec;
+                    wsh[r][v] = st[k];
+                }
+                // the inputs in the form the dot products take (packed fp16 pairs against fp16
+                // weights, as the Q/K/V GEMV rounds them; fp32 against fp32 weights); a vector
+                // past the row end gets zero inputs and adds exact zeros (weights are finite)
+                gemv_detail::YSlice<T> ysl[kPosTile][kLaneVec];
+#pragma unroll
+                for (int t = 0; t < kPosTile; ++t)
+#pragma unroll
+                    for (int k = 0; k < kLaneVec; ++k) {
+                        if (cv + lane + k * kWave < nvec) ysl[t][k].set(yf[t][k], 0);
+                        else ysl[t][k].zero();
+                    }
+                __syncthreads();
+#pragma unroll
+                for (int k = 0; k < kLaneVec; ++k)
 #pragma unroll
                     for (int r = 0; r < kRowTile; ++r) {
-                        float w[E];
-                        unpack<T>(wsh[r][lane + k * kWave], w);
+                        const Vec16 w = wsh[r][lane + k * kWave];
 #pragma unroll
-                        for (int t = 0; t < kPosTile; ++t)
-#pragma unroll
-                            for (int q = 0; q < E / 4; ++q) {
-                                acc[r][t] = fmaf(w[4 * q + 0], ok ? yv[t][k][q].x : 0.f, acc[r][t]);
-                                acc[r][t] = fmaf(w[4 * q + 1], ok ? yv[t][k][q].y : 0.f, acc[r][t]);
-                                acc[r][t] = fmaf(w[4 * q + 2], ok ? yv[t][k][q].z : 0.f, acc[r][t]);
-                                acc[r][t] = fmaf(w[4 * q + 3], ok ? yv[t][k][q].w : 0.f, acc[r][t]);
-                            }
+                        for (int t = 0; t < kPosTile; ++t) acc[r][t] = ysl[t][k].dot(w, acc[r][t]);
                     }
-                }
             }
 #pragma unroll
             for (int r = 0; r < kRowTile; ++r)

@@ -1035,11 +1035,9 @@ djv_status dejavu_stack_decode(const djv_model* m, const djv_layer* layers, int 
     // Unless the caller asks for bitwise-reproducible results, the lookahead stack in the
     // vector-ALU form keeps the residual stream in x itself: the O-projection and MLP-down
     // row-axpys add their products to it with fp32 atomics and the GEMVs that read LN(x)
-    // sum its moments themselves, so no finalize launch follows either projection.  Lazy
-    // K/V (which reads tile statistics) and the matrix-core form use the finalize.
-    bool lazy = false;
-    for (int l = 0; l < L; ++l) lazy = lazy || layers[l].Y != nullptr;
-    const bool in_place = lookahead && !dense && !w.mf.on && !lazy &&
+    // (and lazy K/V's save of the attention input) sum its moments themselves, so no
+    // finalize launch follows either projection.  The matrix-core form uses the finalize.
+    const bool in_place = lookahead && !dense && !w.mf.on &&
                           !g_deterministic.load(std::memory_order_relaxed);
     if (!in_place) DJV_HIP(launch_ln_stats(m->B, m->d, x, w.s_in, sm));
 

@@ -24,6 +24,7 @@ namespace {
 constexpr int kLazyThreads = 256;
 constexpr int kLazyRows = kLazyThreads / kWave;  // waves per block: position phases of a row tile
 constexpr int kSaveBatch = 16;  // values of the saved input per thread in flight
+constexpr int kSaveVals = 16384 / kLazyThreads;  // a whole row per thread set (d <= 16384)
 constexpr int kRowTile = 4;     // output rows per catch-up block
 constexpr int kPosTile = 2;     // positions per catch-up wave and pass
 constexpr int kChunkVec = 256;  // weight vectors per row staged in LDS at a time (16 KiB per tile)
@@ -38,9 +39,49 @@ __global__ __launch_bounds__(kLazyThreads) void lazy_kv_kernel(LazyKvArgs a) {
         // so a plain copy loop would wait for each load in turn)
         const int b = bid;
         float* dst = a.Y + ((size_t)b * a.n_cap + a.n) * a.d;
-        float mean = 0.f, rstd = 1.f;
-        if (!a.in.y) gemv_detail::row_moments(a.in, a.d, b, mean, rstd);
         const float* src = (a.in.y ? a.in.y : a.in.x) + (size_t)b * a.d;
+        float mean = 0.f, rstd = 1.f;
+        if (a.in.own_stats) {
+            // LN of x with its moments summed here, the form the GEMVs that read the in-place
+            // residual stream use (one pass of deviations from the row's first element).  The
+            // row stays in registers: one round of loads (addresses clamped into the row), the
+            // block's sums, then the normalised values stored.
+            __shared__ float part[2][kLazyThreads / kWave];
+            const float sh = src[0];
+            float v[kSaveVals];
+#pragma unroll
+            for (int k = 0; k < kSaveVals; ++k) v[k] = src[min(tid + k * kLazyThreads, a.d - 1)];
+            float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+            for (int k = 0; k < kSaveVals; ++k) {
+                const float t = tid + k * kLazyThreads < a.d ? v[k] - sh : 0.f;
+                s1 += t;
+                s2 = fmaf(t, t, s2);
+            }
+            s1 = wave_sum(s1);
+            s2 = wave_sum(s2);
+            if (lane == 0) {
+                part[0][wv] = s1;
+                part[1][wv] = s2;
+            }
+            __syncthreads();
+            float t1 = 0.f, t2 = 0.f;
+#pragma unroll
+            for (int w = 0; w < kLazyThreads / kWave; ++w) {
+                t1 += part[0][w];
+                t2 += part[1][w];
+            }
+            const float inv_n = 1.0f / (float)a.d, md = t1 * inv_n;
+            mean = sh + md;
+            rstd = 1.0f / sqrtf(fmaxf(t2 * inv_n - md * md, 0.f) + a.in.eps);
+#pragma unroll
+            for (int k = 0; k < kSaveVals; ++k) {
+                const int e = tid + k * kLazyThreads;
+                if (e < a.d) dst[e] = (v[k] - mean) * rstd;
+            }
+            return;
+        }
+        if (!a.in.y) gemv_detail::row_moments(a.in, a.d, b, mean, rstd);
         for (int e0 = tid; e0 < a.d; e0 += kLazyThreads * kSaveBatch) {
             float v[kSaveBatch];
 #pragma unroll
@@ -171,7 +212,8 @@ __global__ __launch_bounds__(kLazyThreads) void lazy_kv_kernel(LazyKvArgs a) {
 hipError_t launch_lazy_kv(bool f16, const LazyKvArgs& a, hipStream_t s) {
     // an empty head list (top-k with k = 0) still saves the step's input and carries the
     // valid lengths over; there is nothing to catch up
-    if (a.B < 1 || a.d < 1 || a.h < 1 || a.n < 0 || a.n >= a.n_cap || a.heads.cap < 0 || a.in.own_stats)
+    if (a.B < 1 || a.d < 1 || a.h < 1 || a.n < 0 || a.n >= a.n_cap || a.heads.cap < 0 ||
+        (a.in.own_stats && (!a.in.x || a.in.y)))
         return hipErrorInvalidValue;
     const long long tiles = (long long)a.heads.cap * 2 * a.dh / kRowTile;  // dh % 4 == 0
     const dim3 grid((unsigned)(a.B + 1 + tiles));

@@ -316,8 +316,8 @@ djv_status dejavu_sparse_layer(const djv_model* m, const djv_layer* layer, float
  *   computes; layer 0's sets are predicted first from LN(x_0).  The overlap is inside
  *   launches on the one stream: the predictor weights stream in the same launches as
  *   layer l's weights and each selection runs in a side block of a later launch.
- *   With lookahead, B <= DJV_MAX_VALU_BATCH (vector ALU), no lazy K/V buffers and
- *   dejavu_set_deterministic off (the default), the residual stream stays in x between
+ *   With lookahead, B <= DJV_MAX_VALU_BATCH (vector ALU) and dejavu_set_deterministic
+ *   off (the default), the residual stream stays in x between
  *   launches: the attention and MLP outputs are added to it with fp32 atomics, so no
  *   reduction launch follows either output projection, and the kernels that read LN(x)
  *   compute its moments themselves.  The order of those additions depends on scheduling,

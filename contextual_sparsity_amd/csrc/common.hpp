@@ -365,7 +365,8 @@ hipError_t launch_select(const SelectJob* jobs, int njobs, int B, hipStream_t s,
 // Lazy K/V of the heads a step does not select (lazykv.hip): saves the step's attention
 // input and recomputes the selected heads' missing K/V from the saved inputs.
 struct LazyKvArgs {
-    RowInput in;             // the layer's attention input (y ready, or x with tile stats)
+    RowInput in;             // the layer's attention input (y ready, x with tile stats, or x whose
+                             // moments the save sums itself: own_stats)
     float* Y;                // [B, n_cap, d] saved inputs
     const int32_t* kv_prev;  // [h] positions with valid K/V before this step
     int32_t* kv_next;        // [h] after it

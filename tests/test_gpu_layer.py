@@ -173,7 +173,8 @@ def test_stack_small(lookahead):
 # per-token top-k sets) make the fused projection launches lay the rows of all their
 # segments end to end and share every block among them.
 @pytest.mark.parametrize("B,mode,t", [(1, dj.DJV_THRESHOLD, 0.6), (3, dj.DJV_THRESHOLD, 0.7),
-                                      (3, dj.DJV_TOPK, None), (2, dj.DJV_TOPK, None)])
+                                      (3, dj.DJV_TOPK, None), (2, dj.DJV_TOPK, None),
+                                      (4, dj.DJV_TOPK, None)])
 def test_stack_device_counts(B, mode, t):
     print(f"lookahead stack with device counts B={B} mode={mode}", flush=True)
     s = synth.LayerShape(d=1032, N=1500, h=6, dh=128, n=300, r=136, dtype="f16", B=B)

@@ -703,7 +703,18 @@ hipError_t dispatch_nv(const GemvArgs& a, int nv, hipStream_t s) {
     if constexpr (TS == 64) {
         switch (nv) {
             DJV_GEMV_CASE(1, 4)
-            DJV_GEMV_CASE(2, 2)
+        case 2: {
+            // one row per group when the launch gives its one-wave teams fewer than six rows
+            // each (the P2 rows of a 16384-neuron predictor: about three per team), so every
+            // team has its rows in flight in fewer, shorter rounds; two rows per group for
+            // longer lists (49152 neurons: about ten per team)
+            long long rows = 0;
+            for (int i = 0; i < a.nseg; ++i) rows += (long long)a.seg[i].list.cap * a.seg[i].rpu;
+            const long long teams = (long long)blocks_per_cu<T, 64, 2, NB, 2, MODE, DYN, OWN>() * device_cus() *
+                                    (BlockOf<MODE>::value / 64);
+            if (rows < 6 * teams) return launch_shape<T, 64, 2, NB, 1, MODE, DYN, OWN>(a, s);
+            return launch_shape<T, 64, 2, NB, 2, MODE, DYN, OWN>(a, s);
+        }
             DJV_GEMV_CASE(3, 2)
         default:
             return hipErrorInvalidValue;

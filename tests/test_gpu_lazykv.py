@@ -123,6 +123,20 @@ def test_lazy_kv_weight_chunks(shape):
                for i in range(shape.h))
 
 
+def test_lazy_kv_saved_input_full_width():
+    # rows as wide as the OPT-175B shape's: in the lookahead stack the save sums LN's moments of
+    # x itself (48 values of the row per thread); every saved input equals LN of its layer input
+    print("lazy K/V saved inputs at d=12288", flush=True)
+    s = synth.LayerShape(d=12288, N=2048, h=4, dh=128, n=64, r=128, dtype="f16")
+    L, T = 2, 3
+    shape, w, K0, V0, steps = _run_steps(s, L, T, 54, lazy=True, lookahead=True, k_A=2, k_M=100)
+    _check(shape, w, K0, V0, steps, L)
+    for l in range(L):
+        Y = host(w[l]["Y"])
+        for t, st in enumerate(steps):
+            assert_close(Y[:, shape.n + t], O.layernorm(st["x_in"][l]), TOL["f32"], (l, t))
+
+
 def test_without_lazy_kv_a_reselected_head_reads_stale_entries():
     # the same steps without lazy K/V: a head that skipped a step attends over the cache's
     # old contents at that position, which differ from the all-heads cache

@@ -20,7 +20,12 @@
 // bits) finds the k-th key; keys equal to it are taken in index order.  The bracket only
 // decides how much work is done, never the result: when the check fails (a sample far
 // off, or heavy ties), and for rows above 49152, the row falls back to a radix select
-// over all keys, reloading them per pass.  Threshold rows are ballots of key > tau.
+// over all keys, reloading them per pass.  Rows of 4097 to 16384 scores skip the sample:
+// every key's top 12 bits go into an exact histogram (16 LDS atomics per thread), which
+// gives the first digit of the k-th key at once; the keys sharing that digit are gathered
+// with their full keys from registers, and two radix passes finish (select_row_hist; one
+// search, no bracket check, no re-read of the candidates, one radix pass fewer).  Threshold
+// rows are ballots of key > tau.
 // Every search for the bin holding a rank is done by one wave over the threads' bin sums
 // (find_bin).  With one row the block compacts the result into the ascending index list
 // and the device-side count; several rows are ORed (in LDS for a side block, or by a
@@ -566,12 +571,86 @@ __device__ __forceinline__ bool select_row_fast(RowShared& S, const SelectJob& J
     return true;
 }
 
+// Top-k of row b (0 < k < n, kMaxCand < n <= 1024 * KPT, KPT <= 16) from one read of the
+// row, the first digit from an exact histogram instead of a sample bracket: the top 12
+// bits of every key (held in registers) are histogrammed, the bin holding the k-th largest
+// key is found, keys above that bin are kept and the keys inside it are gathered into LDS
+// with their full keys for the radix passes over the two lower digits.  Returns false,
+// having written nothing the radix path does not rewrite, when that bin holds more than
+// kMaxCand keys (heavy ties).  (For rows of 48 keys per thread the 48 LDS atomics per
+// thread cost as much as the sample bracket saves, and more where the scores cluster.)
+template <int KPT>
+__device__ __forceinline__ bool select_row_hist(RowShared& S, const SelectJob& J, int b) {
+    static_assert(KPT <= 16, "the full keys stay in registers");
+    const int tid = threadIdx.x, lane = tid % kWave;
+    const int n = J.n_out, words = (n + 31) / 32;
+    gchar* zb = uniform_ptr(J.z + (size_t)b * n);
+    const int slots = (n + kThreads - 1) / kThreads;   // key slots in use (uniform, <= KPT)
+    const int wbase = (tid / kWave) * kWave;            // first index of this wave in a slot
+    const int mine = (n - tid + kThreads - 1) / kThreads;  // slot c is in the row iff c < mine
+
+    uint32_t key[KPT];
+    {
+        float v[KPT];
+#pragma clang loop unroll(full)
+        for (int c = 0; c < KPT; ++c) v[c] = load_score(zb, min(tid + kThreads * c, n - 1));
+#pragma clang loop unroll(full)
+        for (int c = 0; c < KPT; ++c) key[c] = score_key(v[c]);
+    }
+    for (int i = tid; i < kMaxBins + kWave; i += kThreads) S.hist[i] = 0u;
+    for (int w = tid; w < words; w += kThreads) {
+        S.selw[w] = 0u;
+        S.tiew[w] = 0u;
+    }
+    __syncthreads();
+    // slots past the row go to one of the 64 spare bins (one per lane), outside the search
+#pragma clang loop unroll(full)
+    for (int c = 0; c < KPT; ++c)
+        if (c < slots) atomicAdd(&S.hist[c < mine ? (key[c] >> 20) : (uint32_t)(kMaxBins + lane)], 1u);
+    __syncthreads();
+    int rem = J.k;
+    const uint32_t top = (uint32_t)find_bin<4>(S.hist, kMaxBins, rem, S.part, S.sh);
+    const int ncand = (int)S.hist[top];
+    if (ncand > kMaxCand) return false;  // uniform
+
+    // candidates take consecutive LDS slots from a block prefix count of each thread's own
+    int mc = 0;
+#pragma clang loop unroll(full)
+    for (int c = 0; c < KPT; ++c) mc += (c < mine && (key[c] >> 20) == top) ? 1 : 0;
+    int total;
+    int at = block_exclusive_scan<kThreads>(mc, S.wtot, &total);
+    // the thread index, opaque to the compiler: without this it keeps every slot's index
+    // (computed for the loads) alive until here
+    int t_op = tid;
+    asm volatile("" : "+v"(t_op));
+#pragma clang loop unroll(full)
+    for (int c = 0; c < KPT; ++c) {
+        if (c < slots) {
+            const uint32_t d = key[c] >> 20;
+            ballot_words(S.selw, words, kThreads * c + wbase, c < mine && d > top);
+            if (c < mine && d == top) {
+                S.cand[at] = key[c];
+                S.cand_j[at] = t_op + kThreads * c;
+                ++at;
+            }
+        }
+    }
+    __syncthreads();
+    uint32_t prefix = top << 20, pmask = 0xFFF00000u;
+    resolve_candidates(S, ncand, prefix, pmask, rem, 1);
+    __syncthreads();
+    take_ties(S, words, rem);
+    return true;
+}
+
 // The whole selection of row b in one block: keys in registers (rows up to 49152), with
 // the radix path for longer rows and as the fallback.
 __device__ __forceinline__ void select_row_full(RowShared& S, const SelectJob& J, int b) {
     const int n = J.n_out;
     bool done = false;
-    if (n <= 16 * kThreads) done = select_row_fast<16>(S, J, b);
+    if (n <= 16 * kThreads)
+        done = (J.mode != 1 && J.k > 0 && J.k < n && n > kMaxCand) ? select_row_hist<16>(S, J, b)
+                                                                     : select_row_fast<16>(S, J, b);
     else if (n <= 48 * kThreads) done = select_row_fast<48>(S, J, b);
     if (!done) {
         __syncthreads();

@@ -25,7 +25,7 @@ def _gpu_select(z: torch.Tensor, mode, k=0, t=0.5):
     return idx[:c].cpu().numpy()
 
 
-@pytest.mark.parametrize("n", [1, 7, 12, 96, 1000, 3072, 36864, 49152, 65536])
+@pytest.mark.parametrize("n", [1, 7, 12, 96, 1000, 3072, 4097, 12289, 16384, 36864, 49152, 65536])
 def test_topk_normal_scores(n):
     print(f"select topk n={n}", flush=True)
     for B in (1, 3):
@@ -42,7 +42,7 @@ def test_topk_normal_scores(n):
 @pytest.mark.parametrize("alphabet", [(0.0, 1.0), (-0.0, 0.0, 2.5, -1.0), (math.nan, -math.inf, 0.5),
                                       (math.nan, math.nan, 0.5), (1.0, 1.0 + 2 ** -23, 1.0 - 2 ** -24)])
 def test_topk_ties(alphabet):
-    for n in (5, 64, 1031, 49152):
+    for n in (5, 64, 1031, 16384, 49152):
         z = synth.make_scores(2, n, seed=n, alphabet=alphabet).to(DEV)
         zh = z.cpu().numpy()
         for k in (0, 1, 2, n // 3, 20000 % (n + 1), n // 2, n):
@@ -52,6 +52,25 @@ def test_topk_ties(alphabet):
                 assert np.array_equal(got, O.select(zh[:1], O.TOPK, k=k)), (alphabet, n, k)
             got = _gpu_select(z, dj.DJV_TOPK, k=k)
             assert np.array_equal(got, O.select(zh, O.TOPK, k=k)), (alphabet, n, k, "B=2")
+
+
+@pytest.mark.parametrize("n", [4097, 16384])
+def test_topk_dense_cluster(n):
+    # normal scores with a cluster of near-equal values (ties, and keys that differ only in
+    # their low bits) placed so that the k-th largest key falls inside it
+    z = synth.make_scores(2, n, seed=n + 11)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(n)
+    for b in range(2):
+        pos = torch.randperm(n, generator=g)[:2000]
+        z[b, pos] = 3.0 + (torch.arange(2000) % 300).float() * 2.0 ** -22
+    z = z.to(DEV)
+    zh = z.cpu().numpy()
+    for k in (5, 40, 820, 1500, 2000, 2100):
+        got = _gpu_select(z[:1], dj.DJV_TOPK, k=k)
+        assert np.array_equal(got, O.select(zh[:1], O.TOPK, k=k)), (n, k)
+        got = _gpu_select(z, dj.DJV_TOPK, k=k)
+        assert np.array_equal(got, O.select(zh, O.TOPK, k=k)), (n, k, "B=2")
 
 
 def test_topk_golden_row():

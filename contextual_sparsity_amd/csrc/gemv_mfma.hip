@@ -16,7 +16,7 @@
 // fragments per chunk and multiplying them with activation fragments from LDS; 16 waves
 // per compute unit keep the loads in flight.  One block fills a compute unit's LDS, so
 // the grid is one block per compute unit.  Each tile writes one fp32 partial per (slice, row, batch
-// row); a finalize sums the slices in order and applies the segment's epilogue (store,
+// row), four tiles' partials at a time; a finalize sums the slices in order and applies the segment's epilogue (store,
 // ReLU, bias + ReLU, Q/K/V with the cache append).
 #include "gemv.hpp"
 
@@ -92,6 +92,7 @@ __global__ __launch_bounds__(kBlock) void gemv_mfma_kernel(GemvArgs a, MfmaPlan 
     constexpr int BP = BT * 16;
     constexpr int kU = 8;                // weight fragments per chunk
     constexpr int kChunk = kMK * kU;     // columns per chunk
+    constexpr int kGroup = 4;            // tiles whose partials are stored together
     extern __shared__ __align__(16) _Float16 ys[];  // [BP][kc + kPad]
     __shared__ float mom[BP][2];
     const int tid = threadIdx.x, l = tid % kWave;
@@ -153,11 +154,8 @@ __global__ __launch_bounds__(kBlock) void gemv_mfma_kernel(GemvArgs a, MfmaPlan 
                 w[u] = __builtin_nontemporal_load(ptr + k / 8);
             }
         };
-        f4_t acc[BT];
-#pragma unroll
-        for (int t = 0; t < BT; ++t) acc[t] = f4_t{0.f, 0.f, 0.f, 0.f};
         const h8_t zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
-        auto compute = [&](const h8_t (&w)[kU], int ck) {
+        auto compute = [&](f4_t (&acc)[BT], const h8_t (&w)[kU], int ck) {
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
                 const bool in = ck * kChunk + kMK * u < kn;
@@ -168,25 +166,37 @@ __global__ __launch_bounds__(kBlock) void gemv_mfma_kernel(GemvArgs a, MfmaPlan 
                     acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wu, yrow[t][k / 8], acc[t], 0, 0, 0);
             }
         };
-        // per tile: all chunks of the slice, 8 (4) weight fragments in flight per chunk
-        // (other waves cover the latency); the next tile's row is looked up a tile ahead
+        // per tile: all chunks of the slice, 8 weight fragments in flight per chunk (other
+        // waves cover the latency); the next tile's row is looked up a tile ahead.  The
+        // partials of kGroup tiles are kept in registers and stored together: a wave's stores
+        // share the in-order memory counter with its loads, so a load wait after a store also
+        // waits for the store's acknowledgement, slow while the reads saturate HBM.
         gh8_t* P1 = tile_ptr(0);
-        for (int i = 0; i < ntw; ++i) {
-            gh8_t* P0 = P1;
-            P1 = tile_ptr(i + 1);
-            for (int ck = 0; ck < nck; ++ck) {
-                h8_t w[kU];
-                load(w, P0, ck);
-                compute(w, ck);
+        for (int i0 = 0; i0 < ntw; i0 += kGroup) {
+            f4_t acc[kGroup][BT];
+#pragma unroll
+            for (int j = 0; j < kGroup; ++j) {
+#pragma unroll
+                for (int t = 0; t < BT; ++t) acc[j][t] = f4_t{0.f, 0.f, 0.f, 0.f};
+                if (i0 + j < ntw) {  // uniform
+                    gh8_t* P0 = P1;
+                    P1 = tile_ptr(i0 + j + 1);
+                    for (int ck = 0; ck < nck; ++ck) {
+                        h8_t w[kU];
+                        load(w, P0, ck);
+                        compute(acc[j], w, ck);
+                    }
+                }
             }
 #pragma unroll
-            for (int t = 0; t < BT; ++t)
+            for (int j = 0; j < kGroup; ++j)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int rr = (first + i * kWaves) * kTile + 4 * (l / kTile) + q;
-                    if (rr < rows) P[(size_t)rr * p.bpad + 16 * t + l % kTile] = acc[t][q];
-                    acc[t][q] = 0.f;
-                }
+                for (int t = 0; t < BT; ++t)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int rr = (first + (i0 + j) * kWaves) * kTile + 4 * (l / kTile) + q;
+                        if (i0 + j < ntw && rr < rows) P[(size_t)rr * p.bpad + 16 * t + l % kTile] = acc[j][t][q];
+                    }
         }
     }
 }

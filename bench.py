@@ -78,6 +78,11 @@ def parse(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget")
     ap.add_argument("--breakdown", action="store_true", help="time every kernel family")
     ap.add_argument("--no-lookahead", action="store_true", help="serial schedule for any workload")
+    ap.add_argument("--flush", dest="flush", action="store_true", default=None,
+                    help="write a 1 GiB buffer before every timed step (outside its timing) so that no "
+                         "weights are served from the 256 MB Infinity Cache or L2 (default for one-layer "
+                         "workloads, whose weights would otherwise stay cached between steps)")
+    ap.add_argument("--no-flush", dest="flush", action="store_false")
     ap.add_argument("--deterministic", action="store_true",
                     help="bitwise-reproducible lookahead stack (fixed-order reductions, finalize launches)")
     ap.add_argument("--lookahead", action="store_true",
@@ -677,17 +682,39 @@ def main(argv=None) -> int:
         x.copy_(x0)
         dj.dejavu_stack_decode(m, desc, x, lookahead, dense, None, ws, s_main)
 
+    # cache flush between timed steps: a stack of distinct layers streams past the caches by
+    # itself, one layer run again and again would be partly served from them
+    flush = (L == 1) if args.flush is None else args.flush
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if flush else None
+    flush_val = [0]
+
+    def do_flush():
+        if flush_buf is not None:
+            flush_val[0] ^= 0x5A
+            flush_buf.fill_(flush_val[0])
+
     def timed(n, dense=False):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         w0 = time.perf_counter()
-        a.record(s_main)
-        for _ in range(n):
+        if not flush:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(s_main)
+            for _ in range(n):
+                step(dense)
+            b.record(s_main)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / n, (time.perf_counter() - w0) * 1e3 / n
+        # each step between its own events, after a flush outside them; the wall time holds
+        # the flushes too
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in evs:
+            do_flush()
+            a.record(s_main)
             step(dense)
-        b.record(s_main)
+            b.record(s_main)
         torch.cuda.synchronize()
-        return a.elapsed_time(b) / n, (time.perf_counter() - w0) * 1e3 / n
+        return sum(a.elapsed_time(b) for a, b in evs) / n, (time.perf_counter() - w0) * 1e3 / n
 
     for _ in range(args.warmup):
         step()
@@ -702,6 +729,7 @@ def main(argv=None) -> int:
            for _ in range(args.steps)]
     torch.cuda.synchronize()
     for a, b in evs:
+        do_flush()
         a.record(s_main)
         step()
         b.record(s_main)
@@ -716,6 +744,7 @@ def main(argv=None) -> int:
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * cap)]
         dj.dejavu_profile_kernel(fam, evs)
         for _ in range(n_steps):
+            do_flush()
             step()
         used = dj.dejavu_profile_count()
         torch.cuda.synchronize()
@@ -788,7 +817,9 @@ def main(argv=None) -> int:
     log(f"Q/K/V+P1 launch {qkv_ms * 1e3:.1f} us/launch over {qkv_n} launches -> {qkv_gbs:.0f} GB/s")
     kernels = {}
     if args.breakdown:
-        fam_bytes = {"qkv": k1_bytes, "mlp_up": k_M * s.d * e, "mlp_down": k_M * s.d * e,
+        # the MLP launches read the kept (at B > 1: the union's) W1 and W2 rows
+        mlp_half = lb["mlp"] * s.d / (2 * s.d + 1)
+        fam_bytes = {"qkv": k1_bytes, "mlp_up": mlp_half, "mlp_down": mlp_half,
                      "o_proj": lb["o_proj"], "attn": lb["kv"], "pred_1": p1_bytes,
                      "pred_2": (s.N + s.h) * s.r * e, "select": None}
         for fam in ("qkv", "mlp_up", "mlp_down", "o_proj", "attn", "pred_1", "pred_2", "select"):
@@ -865,7 +896,7 @@ def main(argv=None) -> int:
         "config": {"workload": wl.name, "layers": L, "d": s.d, "N": s.N, "h": s.h, "dh": s.dh,
                    "n": s.n, "r": s.r, "batch": s.B, "keep_neurons_pct": wl.pct_M,
                    "keep_heads_pct": wl.pct_A, "k_M": k_M, "k_A": k_A, "lookahead": lookahead,
-                   "deterministic": args.deterministic, "union_sets": unions},
+                   "deterministic": args.deterministic, "union_sets": unions, "cache_flush": flush},
         "us_per_layer": round(ms_step * 1e3 / L, 2),
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "copy_ref_GBps": round(copy_gbs, 1),

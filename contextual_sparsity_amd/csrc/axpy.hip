@@ -434,21 +434,24 @@ __global__ __launch_bounds__(kFinGroups * kFinQuads) void axpy_finalize_kernel(A
 // (here: rows) per lane for one column, while a weight row is contiguous in columns, so
 // the weights go through LDS: coalesced 16-byte row loads in, 16-bit column reads out.
 //
-// A block (4 waves) owns kAxCols = 256 columns, 64 per wave (4 column tiles of 16), and a
-// chunk of rows taken kAxGroup = 64 at a time: the group's weight tile (32 KiB) and its
+// A block (4 waves) owns kAxCols = 512 columns, 128 per wave (8 column tiles of 16), and a
+// chunk of rows taken kAxGroup = 32 at a time: the group's weight tile (32 KiB) and its
 // coefficients sit in LDS while the next group's loads are already in registers.  One
-// coefficient fragment feeds the wave's four column tiles; one weight fragment feeds the
-// BT batch tiles.
+// coefficient fragment feeds the wave's eight column tiles; one weight fragment feeds the
+// BT batch tiles.  Each load instruction reads a 1 KiB run of one row: with 256-column
+// tiles (512-byte runs, the other pieces of each gathered row read by other blocks at other
+// times) the launch ran about 11% slower at batches 16 and 32.
 // ---------------------------------------------------------------------------------
 typedef _Float16 h8m_t __attribute__((ext_vector_type(8)));
 typedef float f4m_t __attribute__((ext_vector_type(4)));
-constexpr int kAxCols = 256;                  // columns per block
+constexpr int kAxCols = 512;                  // columns per block
 constexpr int kAxK = 32;                      // rows per MFMA
-constexpr int kAxGroup = 2 * kAxK;            // rows staged per round
+constexpr int kAxTiles = kAxCols / 4 / 16;    // 16-column tiles per wave
+constexpr int kAxGroup = kAxK;                // rows staged per round
 constexpr int kAxPitch = kAxCols + 4;         // halfs per LDS weight row (8-byte aligned rows)
 constexpr int kAxCfPitch = kAxGroup + 8;      // halfs per LDS coefficient row
 constexpr int kAxLoads = kAxGroup * kAxCols * 2 / 16 / kThreads;  // 16-byte loads per thread per round
-constexpr int kAxTargetBlocks = 1024;         // about four per compute unit (a constant, so that
+constexpr int kAxTargetBlocks = 768;          // about three per compute unit (a constant, so that
                                               // workspace sizes do not depend on the device)
 
 
@@ -479,13 +482,14 @@ __global__ __launch_bounds__(kThreads) void axpy_mfma_kernel(AxpyArgs a) {
     }
     __syncthreads();
 
-    // weight loads: thread t moves columns 8 (t % 32) .. + 8 of rows t / 32 + 8 q
-    const int lc = 8 * (tid % 32), lr = tid / 32;
+    // weight loads: thread t moves columns 8 (t % 64) .. + 8 of rows t / 64 + 4 q (one 1 KiB
+    // run of a row per load instruction)
+    const int lc = 8 * (tid % 64), lr = tid / 64;
     const bool col_ok = c0 + lc + 8 <= a.cols;
     const char* Wb = reinterpret_cast<const char*>(a.W);
     const size_t row_bytes = (size_t)a.cols * 2;
-    // coefficient loads: thread t moves batch row t / 8, group rows 8 (t % 8) .. + 8
-    const int cb = tid / 8, cr = 8 * (tid % 8);
+    // coefficient loads: thread t moves batch row t / 4, group rows 8 (t % 4) .. + 8
+    const int cb = tid / 4, cr = 8 * (tid % 4);
     const int ngroups = (nr + kAxGroup - 1) / kAxGroup;
 
     Vec16 wreg[kAxLoads];
@@ -493,7 +497,7 @@ __global__ __launch_bounds__(kThreads) void axpy_mfma_kernel(AxpyArgs a) {
     auto load_group = [&](int g) {
 #pragma unroll
         for (int q = 0; q < kAxLoads; ++q) {
-            const int i = g * kAxGroup + lr + 8 * q;
+            const int i = g * kAxGroup + lr + 4 * q;
             const int row = i < nr ? row_s[i] : -1;
             const char* p = (row >= 0 && col_ok) ? Wb + (size_t)row * row_bytes + (size_t)(c0 + lc) * 2
                                                  : reinterpret_cast<const char*>(&g_zero16);
@@ -510,19 +514,19 @@ __global__ __launch_bounds__(kThreads) void axpy_mfma_kernel(AxpyArgs a) {
         }
     };
 
-    f4m_t acc[4][BT];
+    f4m_t acc[kAxTiles][BT];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kAxTiles; ++j)
 #pragma unroll
         for (int t = 0; t < BT; ++t) acc[j][t] = f4m_t{0.f, 0.f, 0.f, 0.f};
-    const int kb = 8 * (l / 16), cl = wv * 64 + l % 16;
+    const int kb = 8 * (l / 16), cl = wv * (16 * kAxTiles) + l % 16;
 
     load_group(0);
     for (int g = 0; g < ngroups; ++g) {
 #pragma unroll
         for (int q = 0; q < kAxLoads; ++q) {
             // two 8-byte stores: rows are 8-byte aligned in LDS
-            uint2* dst = reinterpret_cast<uint2*>(&wt[lr + 8 * q][lc]);
+            uint2* dst = reinterpret_cast<uint2*>(&wt[lr + 4 * q][lc]);
             dst[0] = make_uint2(wreg[q].w[0], wreg[q].w[1]);
             dst[1] = make_uint2(wreg[q].w[2], wreg[q].w[3]);
         }
@@ -540,7 +544,7 @@ __global__ __launch_bounds__(kThreads) void axpy_mfma_kernel(AxpyArgs a) {
 #pragma unroll
             for (int t = 0; t < BT; ++t) av[t] = *reinterpret_cast<const h8m_t*>(&cf[16 * t + l % 16][s * kAxK + kb]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < kAxTiles; ++j) {
                 h8m_t bw;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) bw[e] = wt[s * kAxK + kb + e][cl + 16 * j];
@@ -550,9 +554,9 @@ __global__ __launch_bounds__(kThreads) void axpy_mfma_kernel(AxpyArgs a) {
         }
         __syncthreads();
     }
-    // lane l holds D[b = 16 t + 4 (l / 16) + q][column c0 + wv * 64 + 16 j + l % 16]
+    // lane l holds D[b = 16 t + 4 (l / 16) + q][column c0 + cl + 16 j]
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kAxTiles; ++j) {
         const int c = c0 + cl + 16 * j;
         if (c >= a.cols) continue;
 #pragma unroll
